@@ -1,0 +1,8 @@
+"""Plain CPU oracle for MSA decode (test infrastructure only).
+
+Imported by the tests, the smoke entry and the benchmark's CPU-baseline leg;
+never by the GPU library.  See ``oracle.py`` and ``msa_oracle.c``.
+"""
+from .oracle import (OracleProblem, attention, bf16_to_double, build, decode,  # noqa: F401
+                     e2m1_to_double, e4m3_to_double, index_scores, num_threads,
+                     page_table, select)

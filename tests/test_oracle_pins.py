@@ -1,0 +1,401 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: torch's own
+format conversions, the OCP format tables, brute force on tiny inputs, dense
+softmax attention (a library routine) in the cases where MSA reduces to it,
+invariants the pages state (local block kept, 2,048-key cap, positive scale
+invariance, KV read in place through a page view) and the page figures in
+tests/golden/page_figures.json.
+"""
+import json
+import math
+import os
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import CONFIGS, host_arrays, make_workload, small_config
+from tests.refs import (E2M1_TABLE, brute_force_select, decode_bf16, decode_e4m3,
+                        dense_attention, problem_of, token_scores)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_figures.json")
+
+
+def run_oracle(cfg, h, sm_scale=0.0, rows=None):
+    P = problem_of(cfg, sm_scale)
+    return oracle.decode(P, h["q"], h["idx_q"], h["k_pool"], h["v_pool"], h["k_scale"],
+                         h["v_scale"], h["idx_k_pool"], h["block_table"], h["ctx_lens"], rows)
+
+
+def positions(cfg, h):
+    T = cfg.query_len
+    for b in range(cfg.batch):
+        L = int(h["ctx_lens"][b])
+        for t in range(T):
+            yield b, t, b * T + t, L - T + t
+
+
+# ------------------------------------------------------------------ formats
+def test_bf16_decoder_matches_torch_on_all_codes():
+    codes = np.arange(1 << 16, dtype=np.uint16)
+    ref = decode_bf16(codes)
+    got = np.array([oracle.bf16_to_double(int(c)) for c in codes])
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(got))
+    assert np.array_equal(ref[~nan], got[~nan])
+    assert np.array_equal(np.signbit(ref[~nan]), np.signbit(got[~nan]))
+
+
+def test_e4m3_decoder_matches_torch_on_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = decode_e4m3(codes)
+    got = np.array([oracle.e4m3_to_double(int(c)) for c in codes])
+    nan = np.isnan(ref)
+    assert list(np.nonzero(nan)[0]) == [0x7F, 0xFF]
+    assert np.array_equal(nan, np.isnan(got))
+    assert np.array_equal(ref[~nan], got[~nan])
+    assert np.nanmax(got) == 448.0 and np.nanmin(got) == -448.0
+    assert oracle.e4m3_to_double(0x01) == 2.0 ** -9  # smallest subnormal
+
+
+def test_e2m1_decoder_matches_ocp_table():
+    got = [oracle.e2m1_to_double(c) for c in range(16)]
+    assert got == E2M1_TABLE
+    assert [math.copysign(1, g) for g in got] == [math.copysign(1, g) for g in E2M1_TABLE]
+
+
+# ------------------------------------------------------------ block scores
+@pytest.mark.parametrize("kw", [
+    dict(),
+    dict(query_len=3, num_idx_heads=3, ctx_lo=300, ctx_hi=1100, batch=3),
+    dict(idx_dtype="fp8", num_idx_heads=2, ctx_lo=129, ctx_hi=700, batch=3, query_len=2),
+    dict(ctx_list=(1, 127, 128, 129), batch=4, query_len=1),
+])
+def test_block_scores_brute_force(kw):
+    cfg = small_config(**kw)
+    w = make_workload(cfg)
+    h = host_arrays(w)
+    s = oracle.index_scores(problem_of(cfg), h["idx_q"], h["idx_k_pool"], h["block_table"],
+                            h["ctx_lens"])
+    for b, t, r, p in positions(cfg, h):
+        ts = token_scores(cfg, h, b, t)
+        local = p // 128
+        for c in range(cfg.max_blocks):
+            if c > local:
+                assert s[r, c] == -np.inf
+            else:
+                assert s[r, c] == ts[c * 128:min(c * 128 + 128, p + 1)].max()
+
+
+def test_block_score_sums_heads_before_max():
+    """Two index heads whose per-head maxima sit on different tokens: the
+    block score is the max of the head sum, not the sum of head maxima."""
+    cfg = small_config(batch=1, ctx_list=(128,), num_idx_heads=2)
+    w = make_workload(cfg)
+    h = host_arrays(w)
+    ik = np.zeros_like(h["idx_k_pool"])
+    one = np.uint16(0x3F80)  # bf16 1.0
+    ik[0, 0, 5, :] = one     # head 0 likes token 5
+    ik[0, 1, 9, :] = one     # head 1 likes token 9
+    iq = np.full_like(h["idx_q"], one)
+    h["idx_k_pool"], h["idx_q"] = ik, iq
+    s = oracle.index_scores(problem_of(cfg), h["idx_q"], h["idx_k_pool"], h["block_table"],
+                            h["ctx_lens"])
+    assert s[0, 0] == 64.0  # not 128
+
+
+# --------------------------------------------------------------- selection
+@pytest.mark.parametrize("topk", [16, 5, 1])
+@pytest.mark.parametrize("seed", [3, 11])
+def test_selection_brute_force_and_properties(topk, seed):
+    cfg = small_config(batch=3, query_len=2, ctx_lo=1000, ctx_hi=4000, topk=topk, seed=seed,
+                       num_idx_heads=2)
+    w = make_workload(cfg)
+    h = host_arrays(w)
+    res = run_oracle(cfg, h)
+    for b, t, r, p in positions(cfg, h):
+        ts = token_scores(cfg, h, b, t)
+        local = p // 128
+        blk = [ts[c * 128:min(c * 128 + 128, p + 1)].max() for c in range(local + 1)]
+        want = brute_force_select(blk, local, topk)
+        sel = res["selected"][r]
+        n = res["n_selected"][r]
+        assert n == min(topk, local + 1) == len(want)
+        assert list(sel[:n]) == want
+        assert all(sel[n:] == -1)
+        assert local in list(sel[:n])                       # local block always kept
+        assert list(sel[:n]) == sorted(sel[:n])             # ascending
+        chosen = set(sel[:n]) - {local}
+        rest = set(range(local)) - chosen
+        for c in chosen:                                    # every pick beats every miss
+            for d in rest:
+                assert (blk[c], -c) > (blk[d], -d)
+
+
+def test_selection_invariant_under_positive_score_scale():
+    """Scaling every score by the same positive constant keeps the top-k
+    (news.ainew.jp MI355X article, section 2): scale the index queries by 2
+    and 3 (exact in bf16 for integers up to 24)."""
+    cfg = small_config(batch=4, query_len=2, ctx_lo=2500, ctx_hi=6000, num_idx_heads=2, seed=5)
+    w = make_workload(cfg)
+    h = host_arrays(w)
+    base = run_oracle(cfg, h)
+    iqf = decode_bf16(h["idx_q"])
+    for k in (2.0, 3.0):
+        h2 = dict(h)
+        h2["idx_q"] = torch.from_numpy(iqf * k).to(torch.bfloat16).view(torch.int16) \
+            .numpy().view(np.uint16)
+        res = run_oracle(cfg, h2)
+        assert np.array_equal(res["selected"], base["selected"])
+        fin = np.isfinite(base["scores"])
+        assert np.array_equal(res["scores"][fin], k * base["scores"][fin])
+
+
+@pytest.mark.parametrize("copy_to,want", [(3, [1, 5]), (0, [0, 5])])
+def test_selection_ties_go_to_lower_block(copy_to, want):
+    cfg = small_config(batch=1, ctx_list=(6 * 128,), topk=2, permute=True, seed=9)
+    w = make_workload(cfg)
+    h = host_arrays(w)
+    ik = decode_bf16(h["idx_k_pool"]).copy()
+    bt = h["block_table"][0]
+    iq = decode_bf16(h["idx_q"][0])
+    ik[bt[1]] += 4 * np.sign(iq)[:, None, :]                # block 1 becomes the best
+    ik[bt[copy_to]] = ik[bt[1]]                              # an exact tie
+    h["idx_k_pool"] = torch.from_numpy(ik).to(torch.bfloat16).view(torch.int16).numpy() \
+        .view(np.uint16)
+    res = run_oracle(cfg, h)
+    s = res["scores"][0]
+    assert s[1] == s[copy_to] == s[:5].max()
+    assert list(res["selected"][0]) == want
+
+
+@pytest.mark.parametrize("name", ["tiny_4k"])
+def test_planted_blocks_recovered(name):
+    cfg = CONFIGS[name]
+    w = make_workload(cfg)
+    h = host_arrays(w)
+    res = run_oracle(cfg, h)
+    for b in range(cfg.batch):
+        check_planted(res["scores"][b], res["selected"][b], w.planted[b],
+                      (w.ctx_lens[b] - 1) // 128)
+
+
+def check_planted(scores, sel, planted, local):
+    """Planted blocks outrank every unplanted non-local block and are all
+    kept, beside the forced local block; the other slots hold the best of the
+    rest."""
+    sel = list(sel)
+    assert local in sel and set(planted) <= set(sel)
+    others = [c for c in range(local) if c not in planted]
+    assert min(scores[c] for c in planted) > max(scores[c] for c in others)
+    fill = sorted(others, key=lambda c: (-scores[c], c))[:len(sel) - 1 - len(planted)]
+    assert sorted(sel) == sorted(planted + fill + [local])
+
+
+def test_planted_blocks_recovered_multihead_permuted():
+    cfg = small_config(batch=3, ctx_lo=20000, ctx_hi=40000, num_idx_heads=4, num_q_heads=16,
+                       num_kv_heads=2, n_plant=8, seed=21)
+    w = make_workload(cfg)
+    h = host_arrays(w)
+    P = problem_of(cfg)
+    s = oracle.index_scores(P, h["idx_q"], h["idx_k_pool"], h["block_table"], h["ctx_lens"])
+    sel, _ = oracle.select(P, s, h["ctx_lens"])
+    for b in range(cfg.batch):
+        check_planted(s[b], sel[b], w.planted[b], (w.ctx_lens[b] - 1) // 128)
+
+
+def test_planted_overflow_drops_weakest():
+    """16 planted non-local blocks compete for 15 free slots: exactly 15 are
+    kept and the forced local block takes the 16th place."""
+    cfg = small_config(batch=2, ctx_lo=30000, ctx_hi=30000, n_plant=16, seed=4)
+    w = make_workload(cfg)
+    h = host_arrays(w)
+    res = run_oracle(cfg, h)
+    for b in range(cfg.batch):
+        local = (w.ctx_lens[b] - 1) // 128
+        sel = list(res["selected"][b])
+        assert local in sel
+        picked = set(sel) - {local}
+        assert len(picked) == 15 and picked <= set(w.planted[b])
+
+
+def test_key_cap():
+    """At most 16 x 128 = 2,048 keys per query; with a long context exactly
+    15 full blocks plus the causal part of the local block."""
+    gold = json.load(open(GOLDEN))
+    cap = gold["blocks_kept"]["value"] * gold["block_tokens"]["value"]
+    assert cap == gold["max_keys_per_query"]["value"]
+    cfg = small_config(batch=4, query_len=3, ctx_lo=2100, ctx_hi=9000, seed=13)
+    w = make_workload(cfg)
+    h = host_arrays(w)
+    res = run_oracle(cfg, h)
+    for b, t, r, p in positions(cfg, h):
+        sel = res["selected"][r][:res["n_selected"][r]]
+        keys = sum(min(128, p + 1 - c * 128) for c in sel)
+        assert keys <= cap
+        if p // 128 >= 16:
+            assert keys == 15 * 128 + (p % 128) + 1
+
+
+# -------------------------------------------------------------- page table
+def test_page_table_closed_form():
+    cfg = small_config(batch=3, query_len=2, ctx_lo=200, ctx_hi=5000, seed=17)
+    w = make_workload(cfg)
+    h = host_arrays(w)
+    res = run_oracle(cfg, h)
+    for b, t, r, p in positions(cfg, h):
+        sel = res["selected"][r]
+        pt = res["page_table"][r]
+        n = res["n_selected"][r]
+        for k in range(cfg.topk):
+            for j in range(8):
+                want = h["block_table"][b][sel[k]] * 8 + j if k < n else -1
+                assert pt[8 * k + j] == want
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "nvfp4"])
+def test_outputs_invariant_under_physical_permutation(kv):
+    """The page table is a view over KV that stays in place: moving physical
+    blocks and rewriting the block table changes nothing else."""
+    cfg = small_config(batch=3, query_len=2, ctx_lo=2000, ctx_hi=4500, kv_dtype=kv,
+                       num_q_heads=8, num_kv_heads=2, permute=False, seed=23)
+    w = make_workload(cfg)
+    h = host_arrays(w)
+    base = run_oracle(cfg, h)
+    NB = w.num_phys_blocks
+    pi = np.random.default_rng(0).permutation(NB)
+    h2 = dict(h)
+    for key in ("idx_k_pool", "k_pool", "v_pool", "k_scale", "v_scale"):
+        if h[key] is None:
+            continue
+        moved = np.empty_like(h[key])
+        moved[pi] = h[key]
+        h2[key] = moved
+    bt = h["block_table"].copy()
+    for b in range(cfg.batch):
+        bt[b, :w.nblk[b]] = pi[bt[b, :w.nblk[b]]]
+    h2["block_table"] = bt
+    res = run_oracle(cfg, h2)
+    assert np.array_equal(res["selected"], base["selected"])
+    assert np.array_equal(res["scores"], base["scores"])
+    assert np.array_equal(res["out"], base["out"])
+    mapped = np.where(base["page_table"] >= 0,
+                      pi[np.maximum(base["page_table"], 0) // 8] * 8 + base["page_table"] % 8, -1)
+    assert np.array_equal(res["page_table"], mapped)
+
+
+# --------------------------------------------------------------- attention
+@pytest.mark.parametrize("kw", [
+    dict(ctx_list=(1, 77, 128, 129, 2048), batch=5, query_len=1),
+    dict(ctx_list=(3, 700, 2048), batch=3, query_len=3, num_q_heads=16, num_kv_heads=2),
+    dict(ctx_list=(1000, 2048), batch=2, kv_dtype="fp8", query_len=2),
+    dict(ctx_list=(300, 1999), batch=2, kv_dtype="nvfp4", num_q_heads=4, num_kv_heads=4),
+])
+def test_dense_equality_up_to_2048_keys(kw):
+    """With at most 16 causal blocks every block is kept, so MSA equals dense
+    causal attention (softmax in float64 torch)."""
+    cfg = small_config(**kw)
+    w = make_workload(cfg)
+    h = host_arrays(w)
+    res = run_oracle(cfg, h)
+    for b, t, r, p in positions(cfg, h):
+        ref = dense_attention(cfg, h, b, t)
+        assert np.max(np.abs(res["out"][r] - ref)) < 1e-12
+
+
+@pytest.mark.parametrize("kw", [
+    dict(batch=3, query_len=2, ctx_lo=2500, ctx_hi=6000, num_q_heads=16, num_kv_heads=2),
+    dict(batch=2, query_len=1, ctx_lo=3000, ctx_hi=5000, topk=5, kv_dtype="fp8"),
+    dict(batch=2, query_len=3, ctx_lo=2200, ctx_hi=4000, kv_dtype="nvfp4", idx_dtype="fp8",
+         num_idx_heads=2),
+])
+def test_masked_dense_brute_force(kw):
+    """Oracle output equals dense softmax attention restricted, by an explicit
+    mask, to the brute-force selection."""
+    cfg = small_config(seed=31, **kw)
+    w = make_workload(cfg)
+    h = host_arrays(w)
+    res = run_oracle(cfg, h)
+    for b, t, r, p in positions(cfg, h):
+        ts = token_scores(cfg, h, b, t)
+        local = p // 128
+        blk = [ts[c * 128:min(c * 128 + 128, p + 1)].max() for c in range(local + 1)]
+        sel = brute_force_select(blk, local, cfg.topk)
+        ref = dense_attention(cfg, h, b, t, allowed_blocks=sel)
+        assert np.max(np.abs(res["out"][r] - ref)) < 1e-12
+
+
+def test_custom_softmax_scale():
+    cfg = small_config(ctx_list=(900,), batch=1)
+    w = make_workload(cfg)
+    h = host_arrays(w)
+    res = run_oracle(cfg, h, sm_scale=0.3)
+    ref = dense_attention(cfg, h, 0, 0, sm_scale=0.3)
+    assert np.max(np.abs(res["out"][0] - ref)) < 1e-12
+
+
+def test_unselected_blocks_do_not_matter():
+    cfg = small_config(batch=2, ctx_lo=4000, ctx_hi=6000, seed=41)
+    w = make_workload(cfg)
+    h = host_arrays(w)
+    base = run_oracle(cfg, h)
+    h2 = dict(h)
+    k = h["k_pool"].copy()
+    v = h["v_pool"].copy()
+    for b in range(cfg.batch):
+        sel = set(base["selected"][b][:base["n_selected"][b]])
+        for c in range(w.nblk[b]):
+            if c not in sel:
+                k[h["block_table"][b][c]] ^= np.uint16(0x1234)
+                v[h["block_table"][b][c]] ^= np.uint16(0x0F0F)
+    h2["k_pool"], h2["v_pool"] = k, v
+    res = run_oracle(cfg, h2)
+    assert np.array_equal(res["out"], base["out"])
+
+
+def test_row_subset_matches_full_run():
+    cfg = small_config(batch=3, query_len=2, ctx_lo=1800, ctx_hi=4000, seed=43)
+    w = make_workload(cfg)
+    h = host_arrays(w)
+    full = run_oracle(cfg, h)
+    rows = np.array([5, 0, 3], dtype=np.int32)
+    part = run_oracle(cfg, h, rows=rows)
+    for key in ("scores", "selected", "n_selected", "page_table", "out"):
+        assert np.array_equal(part[key], full[key][rows])
+
+
+# ------------------------------------------------------------ page figures
+def test_kv_bytes_per_token_match_page_figures():
+    """The storage layouts reproduce the byte counts the pages print: 61,440
+    bytes per token for fp8 K+V codes and 34,560 for the 4-bit layout (codes
+    plus one e4m3 scale per 16 elements), over 60 layers of 4 KV heads."""
+    gold = json.load(open(GOLDEN))
+    layers = gold["model_layers"]["value"]
+    hkv = gold["heads_q_kv_idx"]["value"][1]
+    per_head = {}
+    for kv in ("fp8", "nvfp4"):
+        cfg = small_config(batch=1, ctx_list=(128,), kv_dtype=kv, num_kv_heads=1,
+                           num_q_heads=1)
+        t = make_workload(cfg).tensors
+        tok = t["k_pool"][0, 0, 0]
+        nbytes = tok.numel() * tok.element_size()
+        if kv == "nvfp4":
+            sc = t["k_scale"][0, 0, 0]
+            nbytes += sc.numel() * sc.element_size()
+        per_head[kv] = 2 * nbytes  # K and V
+    assert per_head["fp8"] * hkv * layers == gold["kv_bytes_per_token_fp8"]["value"]
+    assert per_head["nvfp4"] * hkv * layers == gold["kv_bytes_per_token_nvfp4"]["value"]
+    assert 1 - per_head["nvfp4"] / per_head["fp8"] == pytest.approx(0.4375)
+
+
+def test_config_shapes_follow_page_heads():
+    gold = json.load(open(GOLDEN))
+    full = CONFIGS["layer_128k"]
+    rank = CONFIGS["tp8_rank_32k"]
+    assert [full.num_q_heads, full.num_kv_heads, full.num_idx_heads] == \
+        gold["heads_q_kv_idx"]["value"]
+    assert [rank.num_q_heads, rank.num_kv_heads, rank.num_idx_heads] == \
+        gold["tp8_rank_heads_q_kv_idx"]["value"]
