@@ -1,0 +1,253 @@
+// C ABI of libmsa: argument validation, workspace layout, dispatch records
+// and the entry points declared in include/msa.h.
+#include "msa.h"
+#include "msa_internal.h"
+
+#include <math.h>
+#include <string.h>
+
+#include <string>
+
+namespace msa {
+
+static thread_local int g_last_hip_error = 0;
+static thread_local std::string g_last_dispatch;
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+Workspace workspace_layout(const Dims& d) {
+  const SplitPlan sp = plan_splits(d);
+  const size_t rh = (size_t)d.R() * d.Hq;
+  Workspace w;
+  size_t off = 0;
+  w.part_o = off;
+  off = align256(off + rh * sp.splits * 128 * sizeof(float));
+  w.part_ml = off;
+  off = align256(off + rh * sp.splits * 2 * sizeof(float));
+  w.scores = off;
+  off = align256(off + (size_t)d.R() * d.MAXB * sizeof(float));
+  w.n_selected = off;
+  off = align256(off + (size_t)d.R() * sizeof(int32_t));
+  w.selected = off;
+  off = align256(off + (size_t)d.R() * d.topk * sizeof(int32_t));
+  w.page_table = off;
+  off = align256(off + (size_t)d.R() * d.PT() * sizeof(int32_t));
+  w.total = off;
+  return w;
+}
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Validates the descriptor; fills `d`.
+int check_problem(const msa_problem* p, Dims* d) {
+  if (!p || p->struct_size != sizeof(msa_problem)) return MSA_ERR_INVALID_ARG;
+  if (p->batch < 1 || p->decode_query_len < 1 || p->num_q_heads < 1 || p->num_kv_heads < 1 ||
+      p->num_idx_heads < 1 || p->max_blocks_per_seq < 1 || p->num_phys_blocks < 1 ||
+      p->topk < 1 || p->local_blocks < 0)
+    return MSA_ERR_INVALID_ARG;
+  if (p->num_q_heads % p->num_kv_heads != 0) return MSA_ERR_INVALID_ARG;
+  if (!(p->sm_scale >= 0.f) || !isfinite(p->sm_scale)) return MSA_ERR_INVALID_ARG;
+  if (p->flags != 0) return MSA_ERR_INVALID_ARG;
+  if (p->head_dim != 128 || p->idx_dim != 64 || p->block_size != 128 || p->page_size != 16 ||
+      p->local_blocks != 1 || p->topk > 16 || p->decode_query_len > 16 ||
+      p->num_idx_heads > 16 || p->num_q_heads / p->num_kv_heads > 16)
+    return MSA_ERR_UNSUPPORTED;
+  if (p->kv_dtype < MSA_DTYPE_BF16 || p->kv_dtype > MSA_DTYPE_NVFP4) return MSA_ERR_UNSUPPORTED;
+  if (p->idx_k_dtype != MSA_DTYPE_BF16 && p->idx_k_dtype != MSA_DTYPE_FP8_E4M3)
+    return MSA_ERR_UNSUPPORTED;
+  // grid limits: one wave per (request, block) in the scan
+  if ((long)p->batch * p->max_blocks_per_seq > (1L << 30) ||
+      (long)p->batch * p->decode_query_len * p->num_q_heads > (1L << 30))
+    return MSA_ERR_UNSUPPORTED;
+  d->B = p->batch;
+  d->T = p->decode_query_len;
+  d->Hq = p->num_q_heads;
+  d->Hkv = p->num_kv_heads;
+  d->Hidx = p->num_idx_heads;
+  d->MAXB = p->max_blocks_per_seq;
+  d->NB = p->num_phys_blocks;
+  d->topk = p->topk;
+  d->kv_dtype = p->kv_dtype;
+  d->idx_dtype = p->idx_k_dtype;
+  const float scale = p->sm_scale > 0.f ? p->sm_scale : 1.0f / sqrtf((float)p->head_dim);
+  d->scale_log2 = scale * 1.4426950408889634f;
+  return MSA_OK;
+}
+
+int check_ptr(const void* p) {
+  if (!p) return MSA_ERR_INVALID_ARG;
+  return aligned16(p) ? MSA_OK : MSA_ERR_INVALID_ARG;
+}
+
+int check_index_inputs(const msa_tensors* t) {
+  if (!t) return MSA_ERR_INVALID_ARG;
+  int e;
+  if ((e = check_ptr(t->idx_q)) || (e = check_ptr(t->idx_k_pool)) ||
+      (e = check_ptr(t->block_table)) || (e = check_ptr(t->ctx_lens)))
+    return e;
+  return MSA_OK;
+}
+
+int check_kv_inputs(const Dims& d, const msa_tensors* t) {
+  if (!t) return MSA_ERR_INVALID_ARG;
+  int e;
+  if ((e = check_ptr(t->q)) || (e = check_ptr(t->k_pool)) || (e = check_ptr(t->v_pool)) ||
+      (e = check_ptr(t->ctx_lens)))
+    return e;
+  if (d.kv_dtype != MSA_DTYPE_BF16) {
+    if ((e = check_ptr(t->k_scale)) || (e = check_ptr(t->v_scale))) return e;
+  }
+  return MSA_OK;
+}
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return MSA_OK;
+  g_last_hip_error = (int)e;
+  return MSA_ERR_HIP;
+}
+
+}  // namespace
+}  // namespace msa
+
+using namespace msa;
+
+extern "C" {
+
+int msa_index_score(const msa_problem* p, const msa_tensors* t, float* block_scores,
+                    void* stream) {
+  Dims d;
+  int e;
+  if ((e = check_problem(p, &d))) return e;
+  if ((e = check_index_inputs(t)) || (e = check_ptr(block_scores))) return e;
+  std::string note;
+  e = hip_status(launch_index_scan(d, t->idx_q, t->idx_k_pool, t->block_table, t->ctx_lens,
+                                   block_scores, (hipStream_t)stream, &note));
+  if (e == MSA_OK) g_last_dispatch = note;
+  return e;
+}
+
+int msa_select_blocks(const msa_problem* p, const float* block_scores, const int32_t* ctx_lens,
+                      int32_t* selected, int32_t* n_selected, void* stream) {
+  Dims d;
+  int e;
+  if ((e = check_problem(p, &d))) return e;
+  if ((e = check_ptr(block_scores)) || (e = check_ptr(ctx_lens)) || (e = check_ptr(selected)) ||
+      (e = check_ptr(n_selected)))
+    return e;
+  std::string note;
+  e = hip_status(launch_select(d, block_scores, ctx_lens, nullptr, selected, n_selected, nullptr,
+                               (hipStream_t)stream, &note));
+  if (e == MSA_OK) g_last_dispatch = note;
+  return e;
+}
+
+int msa_build_page_table(const msa_problem* p, const int32_t* selected,
+                         const int32_t* block_table, int32_t* page_table, void* stream) {
+  Dims d;
+  int e;
+  if ((e = check_problem(p, &d))) return e;
+  if ((e = check_ptr(selected)) || (e = check_ptr(block_table)) || (e = check_ptr(page_table)))
+    return e;
+  std::string note;
+  e = hip_status(launch_page_table(d, selected, block_table, page_table, (hipStream_t)stream,
+                                   &note));
+  if (e == MSA_OK) g_last_dispatch = note;
+  return e;
+}
+
+size_t msa_workspace_bytes(const msa_problem* p) {
+  Dims d;
+  if (check_problem(p, &d)) return 0;
+  return workspace_layout(d).total;
+}
+
+int msa_sparse_decode(const msa_problem* p, const msa_tensors* t, const int32_t* page_table,
+                      float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  Dims d;
+  int e;
+  if ((e = check_problem(p, &d))) return e;
+  if ((e = check_kv_inputs(d, t)) || (e = check_ptr(page_table)) || (e = check_ptr(out)) ||
+      (e = check_ptr(workspace)))
+    return e;
+  const Workspace w = workspace_layout(d);
+  if (workspace_bytes < w.total) return MSA_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  std::string note;
+  e = hip_status(launch_sparse_attention(d, t->q, t->k_pool, t->v_pool, t->k_scale, t->v_scale,
+                                         page_table, t->ctx_lens,
+                                         reinterpret_cast<float*>(ws + w.part_o),
+                                         reinterpret_cast<float*>(ws + w.part_ml), out,
+                                         (hipStream_t)stream, &note));
+  if (e == MSA_OK) g_last_dispatch = note;
+  return e;
+}
+
+int msa_decode(const msa_problem* p, const msa_tensors* t, int32_t* selected,
+               int32_t* page_table, float* out, void* workspace, size_t workspace_bytes,
+               void* stream) {
+  Dims d;
+  int e;
+  if ((e = check_problem(p, &d))) return e;
+  if ((e = check_index_inputs(t)) || (e = check_kv_inputs(d, t)) || (e = check_ptr(out)) ||
+      (e = check_ptr(workspace)))
+    return e;
+  if ((selected && !aligned16(selected)) || (page_table && !aligned16(page_table)))
+    return MSA_ERR_INVALID_ARG;
+  const Workspace w = workspace_layout(d);
+  if (workspace_bytes < w.total) return MSA_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  float* scores = reinterpret_cast<float*>(ws + w.scores);
+  int32_t* nsel = reinterpret_cast<int32_t*>(ws + w.n_selected);
+  int32_t* sel = selected ? selected : reinterpret_cast<int32_t*>(ws + w.selected);
+  int32_t* pt = page_table ? page_table : reinterpret_cast<int32_t*>(ws + w.page_table);
+  hipStream_t s = (hipStream_t)stream;
+  std::string note;
+  if ((e = hip_status(launch_index_scan(d, t->idx_q, t->idx_k_pool, t->block_table, t->ctx_lens,
+                                        scores, s, &note))))
+    return e;
+  note += " ";
+  if ((e = hip_status(launch_select(d, scores, t->ctx_lens, t->block_table, sel, nsel, pt, s,
+                                    &note))))
+    return e;
+  note += " ";
+  if ((e = hip_status(launch_sparse_attention(d, t->q, t->k_pool, t->v_pool, t->k_scale,
+                                              t->v_scale, pt, t->ctx_lens,
+                                              reinterpret_cast<float*>(ws + w.part_o),
+                                              reinterpret_cast<float*>(ws + w.part_ml), out, s,
+                                              &note))))
+    return e;
+  g_last_dispatch = note;
+  return MSA_OK;
+}
+
+const char* msa_status_string(int status) {
+  switch (status) {
+    case MSA_OK: return "ok";
+    case MSA_ERR_INVALID_ARG: return "invalid argument";
+    case MSA_ERR_UNSUPPORTED: return "unsupported dtype or shape";
+    case MSA_ERR_WORKSPACE: return "workspace too small";
+    case MSA_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int msa_last_hip_error(void) { return g_last_hip_error; }
+
+int msa_last_dispatch(char* buf, size_t n) {
+  const std::string& s = g_last_dispatch;
+  if (buf && n > 0) {
+    const size_t k = s.size() < n - 1 ? s.size() : n - 1;
+    memcpy(buf, s.data(), k);
+    buf[k] = '\0';
+  }
+  return (int)s.size();
+}
+
+int msa_selftest_decoders(float* out, void* stream) {
+  if (check_ptr(out)) return MSA_ERR_INVALID_ARG;
+  return hip_status(launch_selftest_decoders(out, (hipStream_t)stream));
+}
+
+}  // extern "C"

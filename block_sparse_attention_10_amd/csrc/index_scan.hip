@@ -1,0 +1,183 @@
+// Step 1 of MSA decode: block scoring by the index heads.
+//
+// agentlenshq page "MiniMax M3 vLLM サポート", section "MSA 実行プロセス",
+// step 1: small index heads score every candidate 128-token KV block.  The
+// block score is the maximum, over the block's tokens that are causal to the
+// row, of the index dot product summed over index heads.  news.ainew.jp
+// MI355X article, section 2: one indexer pass per request covers every draft
+// position, so each key load is reused by all T rows.
+//
+// Design (gfx950): this is a matrix-vector stream, not a dense contraction,
+// so it runs on the VALU.  One wave scores one logical block for all rows of
+// its request: every load instruction moves 1 KB of contiguous keys (64
+// lanes x 16 B); bf16 keys feed v_dot2_f32_bf16 directly, fp8 keys are
+// widened to bf16 pairs in registers first.  Index queries and keys hold
+// small integers, so every fp32 partial sum is exact in any order.  The lanes
+// that share a token are folded by a transpose-reduce (each butterfly stage
+// halves the partials a lane carries), then the wave takes the causal max.
+#include "msa_device.h"
+#include "msa_internal.h"
+
+#include <math.h>
+
+namespace msa {
+namespace {
+
+constexpr int kBlock = 128;  // tokens per KV block
+constexpr int kIdxDim = 64;  // index head dimension
+
+// One butterfly stage of the transpose-reduce: lanes with `MASK` set keep
+// the upper half of their partials, the others the lower half, and each adds
+// its partner's copy of the half it keeps.
+template <int HALF, int MASK>
+__device__ __forceinline__ void fold_stage(float* v, int lane) {
+  const bool up = (lane & MASK) != 0;
+#pragma unroll
+  for (int j = 0; j < HALF; ++j) {
+    const float send = up ? v[j] : v[j + HALF];
+    const float keep = up ? v[j + HALF] : v[j];
+    v[j] = keep + __shfl_xor(send, MASK);
+  }
+}
+
+// KB: bytes per key element (2 = bf16, 1 = fp8 e4m3).  TR: rows scored per
+// pass (1, 2 or 4); more rows loop over passes.
+template <int KB, int TR>
+__global__ __launch_bounds__(256) void index_scan_kernel(
+    const uint16_t* __restrict__ idx_q, const uint8_t* __restrict__ idx_k,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ ctx_lens,
+    float* __restrict__ scores, int B, int T, int Hidx, int MAXB) {
+  constexpr int DPL = 16 / KB;       // dims per lane per load (8 / 16)
+  constexpr int LPT = kIdxDim / DPL; // lanes per token (8 / 4)
+  constexpr int TPL = kWave / LPT;   // tokens per load instruction (8 / 16)
+  constexpr int NLD = kBlock / TPL;  // loads per (block, head) (16 / 8)
+  constexpr int QW = DPL / 2;        // query dwords per lane per row (4 / 8)
+  static_assert(NLD == 2 * LPT, "transpose-reduce leaves two tokens per lane");
+
+  const int lane = lane_id();
+  const int item = blockIdx.x * 4 + wave_id();
+  if (item >= B * MAXB) return;
+  const int b = item / MAXB;
+  const int c = item - b * MAXB;
+  const int L = ctx_lens[b];
+  float* srow = scores + (size_t)b * T * MAXB + c;
+  if (c * kBlock > L - 1) {  // past the last token: -inf for every row
+    for (int t = lane; t < T; t += kWave) srow[(size_t)t * MAXB] = -INFINITY;
+    return;
+  }
+  const size_t head_bytes = (size_t)kBlock * kIdxDim * KB;
+  const uint8_t* kblk =
+      idx_k + (size_t)block_table[(size_t)b * MAXB + c] * Hidx * head_bytes + lane * 16;
+  const int dim0 = (lane % LPT) * DPL;
+
+  for (int t0 = 0; t0 < T; t0 += TR) {
+    float part[TR][NLD];
+#pragma unroll
+    for (int t = 0; t < TR; ++t)
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) part[t][i] = 0.f;
+
+    for (int h = 0; h < Hidx; ++h) {
+      u32x4 kv[NLD];
+      const uint8_t* kh = kblk + (size_t)h * head_bytes;
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) kv[i] = ldg128(kh + i * 1024);
+      uint32_t qv[TR][QW];
+#pragma unroll
+      for (int t = 0; t < TR; ++t) {
+        const int row = b * T + min(t0 + t, T - 1);
+        const uint16_t* qp = idx_q + ((size_t)row * Hidx + h) * kIdxDim + dim0;
+#pragma unroll
+        for (int w = 0; w < QW; w += 4) {
+          u32x4 v = ldg128(qp + 2 * w);
+          qv[t][w] = v.x; qv[t][w + 1] = v.y; qv[t][w + 2] = v.z; qv[t][w + 3] = v.w;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        uint32_t kw[QW];
+        if constexpr (KB == 2) {
+          kw[0] = kv[i].x; kw[1] = kv[i].y; kw[2] = kv[i].z; kw[3] = kv[i].w;
+        } else {
+          const uint32_t src[4] = {kv[i].x, kv[i].y, kv[i].z, kv[i].w};
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            kw[2 * w] = e4m3x2_to_bf16x2<false>(src[w]);
+            kw[2 * w + 1] = e4m3x2_to_bf16x2<true>(src[w]);
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < TR; ++t) {
+          float acc = part[t][i];
+#pragma unroll
+          for (int w = 0; w < QW; ++w) acc = dot2_bf16(kw[w], qv[t][w], acc);
+          part[t][i] = acc;
+        }
+      }
+    }
+
+#pragma unroll
+    for (int t = 0; t < TR; ++t) {
+      if (t0 + t >= T) break;
+      float* v = part[t];
+      if constexpr (LPT == 8) {
+        fold_stage<8, 4>(v, lane);
+        fold_stage<4, 2>(v, lane);
+        fold_stage<2, 1>(v, lane);
+      } else {
+        fold_stage<4, 2>(v, lane);
+        fold_stage<2, 1>(v, lane);
+      }
+      // lane now holds the full scores of loads i = 2 * (lane % LPT) + e
+      const int pos = L - T + t0 + t;
+      float best = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int tok = (2 * (lane % LPT) + e) * TPL + lane / LPT;
+        if (c * kBlock + tok <= pos) best = fmaxf(best, v[e]);
+      }
+      best = wave_max(best);
+      if (lane == 0) srow[(size_t)(t0 + t) * MAXB] = best;
+    }
+  }
+}
+
+template <int KB>
+hipError_t launch_kb(const Dims& d, const void* idx_q, const void* idx_k,
+                     const int32_t* bt, const int32_t* cl, float* scores, hipStream_t s,
+                     std::string* note) {
+  const long items = (long)d.B * d.MAXB;
+  const dim3 grid((unsigned)((items + 3) / 4)), block(256);
+  const auto* q = static_cast<const uint16_t*>(idx_q);
+  const auto* k = static_cast<const uint8_t*>(idx_k);
+  int tr;
+  if (d.T == 1) {
+    tr = 1;
+    hipLaunchKernelGGL((index_scan_kernel<KB, 1>), grid, block, 0, s, q, k, bt, cl, scores, d.B,
+                       d.T, d.Hidx, d.MAXB);
+  } else if (d.T == 2) {
+    tr = 2;
+    hipLaunchKernelGGL((index_scan_kernel<KB, 2>), grid, block, 0, s, q, k, bt, cl, scores, d.B,
+                       d.T, d.Hidx, d.MAXB);
+  } else {
+    tr = 4;
+    hipLaunchKernelGGL((index_scan_kernel<KB, 4>), grid, block, 0, s, q, k, bt, cl, scores, d.B,
+                       d.T, d.Hidx, d.MAXB);
+  }
+  if (note)
+    *note += std::string("index_scan<") + (KB == 2 ? "bf16" : "fp8") + ",rows" +
+             std::to_string(tr) + ">[grid=" + std::to_string(grid.x) + "x256]";
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_index_scan(const Dims& d, const void* idx_q, const void* idx_k,
+                             const int32_t* block_table, const int32_t* ctx_lens,
+                             float* scores, hipStream_t s, std::string* note) {
+  if (d.idx_dtype == 0)
+    return launch_kb<2>(d, idx_q, idx_k, block_table, ctx_lens, scores, s, note);
+  return launch_kb<1>(d, idx_q, idx_k, block_table, ctx_lens, scores, s, note);
+}
+
+}  // namespace msa

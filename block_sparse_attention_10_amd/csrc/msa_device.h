@@ -1,0 +1,94 @@
+// Device helpers for the gfx950 (CDNA4) MSA kernels: vector types, bf16 /
+// fp8 / fp4 conversions, wave-level reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msa {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// Wave index inside the workgroup, made provably uniform for the compiler.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+}
+
+__device__ __forceinline__ u32x4 ldg128(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+// fp32 += a.x * b.x + a.y * b.y over packed bf16 pairs (v_dot2_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                         __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// Two OCP E4M3 codes (16-bit half HI of `codes`) -> packed bf16 pair.
+// Exact: every E4M3 value is a bf16 value.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t codes) {
+  return __builtin_bit_cast(uint32_t,
+                            __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, HI));
+}
+
+// One OCP E4M3 code (low byte of `code`) -> fp32.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
+  f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(code & 0xFFu, 1.0f, false);
+  return v.x;
+}
+
+// Byte `sel` of `packed` holds two OCP E2M1 codes (element 2j in the low
+// nibble, 2j+1 in the high nibble) -> the two values as fp32.
+__device__ __forceinline__ f32x2 e2m1x2_to_f32x2(uint32_t packed, int sel) {
+  switch (sel) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, 1.0f, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, 1.0f, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, 1.0f, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, 1.0f, 3);
+  }
+}
+
+// Pack the upper halves of two fp32 values into a bf16 pair (truncation).
+// Exact whenever the values carry at most 8 significant bits, as decoded
+// fp8 codes and e2m1 x e4m3 products do.
+__device__ __forceinline__ uint32_t pack_bf16_trunc(float lo, float hi) {
+  return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, hi),
+                               __builtin_bit_cast(uint32_t, lo), 0x07060302u);
+}
+
+// Round-to-nearest-even fp32 -> bf16 bits (finite inputs).
+__device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
+  uint32_t u = __builtin_bit_cast(uint32_t, x);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+  return __builtin_bit_cast(float, b << 16);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
+  return v;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    uint64_t o = __shfl_xor(v, m);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+}  // namespace msa

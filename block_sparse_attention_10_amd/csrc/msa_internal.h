@@ -1,0 +1,58 @@
+// Host-side launchers shared by the translation units of libmsa.  Each
+// kernel file owns its kernels and exposes one launcher; api.hip validates
+// arguments, lays out the workspace and calls them.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <string>
+
+namespace msa {
+
+// Dimensions of one call, already validated.
+struct Dims {
+  int B, T, Hq, Hkv, Hidx, MAXB, NB, topk;
+  int kv_dtype, idx_dtype;
+  float scale_log2;  // softmax scale * log2(e)
+  int R() const { return B * T; }
+  int G() const { return Hq / Hkv; }
+  int PT() const { return topk * 8; }  // page-table row length
+};
+
+// Attention split plan: a workgroup of 4 waves covers 4 * cpw chunks of 32
+// keys (two 16-token pages) of one (row, KV head); `splits` workgroups per
+// (row, KV head) together cover the row's page table.
+struct SplitPlan {
+  int cpw;     // chunks per wave
+  int splits;  // workgroups per (row, KV head)
+};
+SplitPlan plan_splits(const Dims& d);
+
+// Workspace carve-up (byte offsets, 256-aligned).
+struct Workspace {
+  size_t part_o, part_ml, scores, n_selected, selected, page_table, total;
+};
+Workspace workspace_layout(const Dims& d);
+
+hipError_t launch_index_scan(const Dims& d, const void* idx_q, const void* idx_k,
+                             const int32_t* block_table, const int32_t* ctx_lens,
+                             float* scores, hipStream_t s, std::string* note);
+
+hipError_t launch_select(const Dims& d, const float* scores, const int32_t* ctx_lens,
+                         const int32_t* block_table, int32_t* selected, int32_t* n_selected,
+                         int32_t* page_table, hipStream_t s, std::string* note);
+
+hipError_t launch_page_table(const Dims& d, const int32_t* selected, const int32_t* block_table,
+                             int32_t* page_table, hipStream_t s, std::string* note);
+
+hipError_t launch_sparse_attention(const Dims& d, const void* q, const void* k_pool,
+                                   const void* v_pool, const void* k_scale,
+                                   const void* v_scale, const int32_t* page_table,
+                                   const int32_t* ctx_lens, float* part_o, float* part_ml,
+                                   float* out, hipStream_t s, std::string* note);
+
+hipError_t launch_selftest_decoders(float* out, hipStream_t s);
+
+}  // namespace msa

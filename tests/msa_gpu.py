@@ -1,0 +1,180 @@
+"""Helpers for the GPU tests: run the library through its C ABI on a
+synthetic workload, and compute oracle results for sampled rows.
+
+The oracle side only ever sees generator outputs (gathered on the device by
+torch indexing and copied to the host) and its own selections; nothing the
+GPU library produced feeds it.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import block_sparse_attention_10_amd as msa
+import oracle
+from synth import Workload
+from tests.refs import problem_of
+
+TOL = {"bf16": 2e-3, "fp8": 1e-2, "nvfp4": 1e-2}
+
+
+def problem_for(w: Workload, **over):
+    c = w.cfg
+    kw = dict(topk=c.topk)
+    kw.update(over)
+    return msa.problem(c.batch, c.query_len, c.num_q_heads, c.num_kv_heads, c.num_idx_heads,
+                       c.max_blocks, w.num_phys_blocks, c.kv_dtype, c.idx_dtype, **kw)
+
+
+def tensors_for(w: Workload):
+    t = w.tensors
+    return msa.tensors(q=t["q"], idx_q=t["idx_q"], k_pool=t["k_pool"], v_pool=t["v_pool"],
+                       k_scale=t["k_scale"], v_scale=t["v_scale"], idx_k_pool=t["idx_k_pool"],
+                       block_table=t["block_table"], ctx_lens=t["ctx_lens"])
+
+
+def alloc_outputs(w: Workload, p):
+    c = w.cfg
+    dev = w.device
+    R = c.rows
+    return {
+        "scores": torch.empty((R, c.max_blocks), dtype=torch.float32, device=dev),
+        "selected": torch.empty((R, c.topk), dtype=torch.int32, device=dev),
+        "n_selected": torch.empty((R,), dtype=torch.int32, device=dev),
+        "page_table": torch.empty((R, c.topk * 8), dtype=torch.int32, device=dev),
+        "out": torch.empty((R, c.num_q_heads, 128), dtype=torch.float32, device=dev),
+        "workspace": torch.empty((msa.msa_workspace_bytes(p),), dtype=torch.uint8, device=dev),
+    }
+
+
+def run_stages(w: Workload, stream=None):
+    """Each entry point on its own, chained through device buffers."""
+    p = problem_for(w)
+    t = tensors_for(w)
+    o = alloc_outputs(w, p)
+    msa.msa_index_score(p, t, o["scores"], stream)
+    msa.msa_select_blocks(p, o["scores"], w.tensors["ctx_lens"], o["selected"], o["n_selected"],
+                          stream)
+    msa.msa_build_page_table(p, o["selected"], w.tensors["block_table"], o["page_table"], stream)
+    msa.msa_sparse_decode(p, t, o["page_table"], o["out"], o["workspace"], stream)
+    torch.cuda.synchronize()
+    return o
+
+
+def run_fused(w: Workload, stream=None, export=True):
+    p = problem_for(w)
+    t = tensors_for(w)
+    o = alloc_outputs(w, p)
+    sel = o["selected"] if export else None
+    pt = o["page_table"] if export else None
+    msa.msa_decode(p, t, sel, pt, o["out"], o["workspace"], stream)
+    torch.cuda.synchronize()
+    del o["scores"], o["n_selected"]  # internal to the fused call
+    if not export:
+        del o["selected"], o["page_table"]
+    return o
+
+
+def _host(x: torch.Tensor) -> np.ndarray:
+    x = x.detach().to("cpu")
+    if x.dtype == torch.bfloat16:
+        return x.view(torch.int16).numpy().view(np.uint16)
+    return x.numpy()
+
+
+def oracle_rows(w: Workload, rows):
+    """Oracle results for the given rows, computed request by request on
+    compact host copies of just the blocks the oracle needs."""
+    c = w.cfg
+    T = c.query_len
+    t = w.tensors
+    bt_all = t["block_table"]
+    res = {}
+    by_req = {}
+    for r in rows:
+        by_req.setdefault(r // T, []).append(r)
+    for b, rs in by_req.items():
+        L = w.ctx_lens[b]
+        nblk = w.nblk[b]
+        bt_row = bt_all[b, :nblk].to(torch.int64)
+        local_rows = np.array([r % T for r in rs], dtype=np.int32)
+        mini = problem_of(c)
+        mini.batch = 1
+        mini.max_blocks = nblk
+        idx = {
+            "idx_q": _host(t["idx_q"][b * T:(b + 1) * T]),
+            "idx_k_pool": _host(t["idx_k_pool"][bt_row]),
+            "bt": np.arange(nblk, dtype=np.int32)[None, :],
+            "ctx": np.array([L], dtype=np.int32),
+        }
+        s = oracle.index_scores(mini, idx["idx_q"], idx["idx_k_pool"], idx["bt"], idx["ctx"],
+                                local_rows)
+        sel, nsel = oracle.select(mini, s, idx["ctx"], local_rows)
+        pt = oracle.page_table(mini, sel, _host(bt_all[b:b + 1, :nblk]), local_rows)
+        # attention on a pool holding only the selected blocks
+        used = sorted({int(x) for x in sel.reshape(-1) if x >= 0})
+        remap = np.zeros(nblk, dtype=np.int32)
+        remap[used] = np.arange(len(used), dtype=np.int32)
+        phys = bt_row[torch.tensor(used, dtype=torch.int64, device=bt_row.device)]
+        kv = {}
+        for name in ("k_pool", "v_pool", "k_scale", "v_scale"):
+            kv[name] = None if t[name] is None else _host(t[name][phys])
+        out = oracle.attention(mini, _host(t["q"][b * T:(b + 1) * T]), kv["k_pool"],
+                               kv["v_pool"], kv["k_scale"], kv["v_scale"], remap[None, :],
+                               idx["ctx"], sel, local_rows)
+        for i, r in enumerate(rs):
+            res[r] = {"scores": s[i], "selected": sel[i], "n_selected": int(nsel[i]),
+                      "page_table": pt[i], "out": out[i]}
+    return res
+
+
+def compare_rows(w: Workload, got, rows, ref=None):
+    """Bit-exact scores / selection / page table, tolerance on outputs."""
+    c = w.cfg
+    ref = ref if ref is not None else oracle_rows(w, rows)
+    tol = TOL[c.kv_dtype]
+    sc = got["scores"][rows].cpu().numpy() if "scores" in got else None
+    sel = got["selected"][rows].cpu().numpy()
+    pt = got["page_table"][rows].cpu().numpy()
+    out = got["out"][rows].cpu().numpy()
+    nsel = got["n_selected"][rows].cpu().numpy() if "n_selected" in got else None
+    worst = 0.0
+    for i, r in enumerate(rows):
+        e = ref[r]
+        nb = e["scores"].shape[0]
+        if sc is not None:
+            assert np.array_equal(sc[i][:nb].astype(np.float64), e["scores"]), f"scores row {r}"
+            assert np.all(np.isneginf(sc[i][nb:])), f"scores tail row {r}"
+        assert np.array_equal(sel[i], e["selected"]), f"selected row {r}"
+        if nsel is not None:
+            assert nsel[i] == e["n_selected"], f"n_selected row {r}"
+        assert np.array_equal(pt[i], e["page_table"]), f"page_table row {r}"
+        err = float(np.max(np.abs(out[i].astype(np.float64) - e["out"])))
+        worst = max(worst, err)
+        assert err <= tol, f"out row {r}: max abs err {err} > {tol}"
+    return worst
+
+
+def check_invariants(w: Workload, got):
+    """Properties every row must satisfy, checked for the whole batch."""
+    c = w.cfg
+    T = c.query_len
+    sel = got["selected"].cpu().numpy()
+    pt = got["page_table"].cpu().numpy()
+    bt = w.tensors["block_table"].cpu().numpy()
+    for r in range(c.rows):
+        b, t = divmod(r, T)
+        pos = w.ctx_lens[b] - T + t
+        local = pos // 128
+        n = min(c.topk, local + 1)
+        s = sel[r]
+        assert np.all(s[n:] == -1) and np.all(s[:n] >= 0)
+        assert s[n - 1] == local, f"row {r}: local block missing"
+        assert np.all(np.diff(s[:n]) > 0), f"row {r}: not ascending"
+        want = np.full(c.topk * 8, -1, dtype=np.int64)
+        want[:n * 8] = (bt[b, s[:n]][:, None] * 8 + np.arange(8)[None, :]).reshape(-1)
+        assert np.array_equal(pt[r], want), f"row {r}: page table"
+        keys = sum(min(128, pos + 1 - int(x) * 128) for x in s[:n])
+        assert keys <= 2048
+    out = got["out"]
+    assert torch.isfinite(out).all()

@@ -1,0 +1,161 @@
+"""GPU parity: the HIP path against the CPU oracle, through the C ABI.
+
+Block scores, selections and page tables must match bit for bit (index
+queries and keys are small integers, so every score is exact); attention
+outputs must be within max-abs 2e-3 of the fp64 oracle for bf16 KV and 1e-2
+for fp8 / 4-bit KV.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_10_amd as msa
+import oracle
+from synth import CONFIG_ORDER, CONFIGS, make_workload, small_config
+from tests.msa_gpu import (TOL, check_invariants, compare_rows, oracle_rows, problem_for,
+                           run_fused, run_stages, tensors_for)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def test_device_decoders_match_oracle():
+    out = torch.empty(544, dtype=torch.float32, device=DEV)
+    msa.msa_selftest_decoders(out)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy().astype(np.float64)
+    e4 = np.array([oracle.e4m3_to_double(c) for c in range(256)])
+    e2 = np.array([oracle.e2m1_to_double(c) for c in range(16)])
+    for base in (0, 288):
+        got = o[base:base + 256]
+        nan = np.isnan(e4)
+        assert np.array_equal(np.isnan(got), nan), f"NaN codes differ (base {base})"
+        assert np.array_equal(got[~nan], e4[~nan]), f"e4m3 decode differs (base {base})"
+    assert np.array_equal(o[256:272], e2), "e2m1 low nibble"
+    assert np.array_equal(o[272:288], e2), "e2m1 high nibble"
+
+
+SMALL = [
+    dict(),
+    dict(batch=3, query_len=1, ctx_lo=1, ctx_hi=700, seed=2),
+    dict(batch=4, query_len=3, ctx_lo=2000, ctx_hi=9000, num_q_heads=16, num_kv_heads=2,
+         num_idx_heads=2, seed=3),
+    dict(batch=5, query_len=2, ctx_lo=2, ctx_hi=5000, kv_dtype="fp8", idx_dtype="fp8", seed=4),
+    dict(batch=2, query_len=4, ctx_lo=4000, ctx_hi=20000, kv_dtype="fp8", idx_dtype="fp8",
+         seed=5),
+    dict(batch=3, query_len=1, ctx_lo=3000, ctx_hi=40000, kv_dtype="nvfp4", idx_dtype="fp8",
+         num_q_heads=64, num_kv_heads=4, num_idx_heads=4, n_plant=16, seed=6),
+    dict(batch=2, query_len=5, ctx_lo=5, ctx_hi=3000, num_q_heads=4, num_kv_heads=4, seed=7),
+    dict(batch=2, query_len=1, ctx_list=(128, 2049), topk=4, seed=8),
+    dict(batch=3, query_len=2, ctx_list=(2, 256, 1280), topk=1, seed=9),
+    dict(batch=1, query_len=16, ctx_list=(4096,), num_q_heads=16, num_kv_heads=1,
+         num_idx_heads=16, seed=10),
+]
+
+
+@pytest.mark.parametrize("kw", SMALL, ids=[str(i) for i in range(len(SMALL))])
+def test_small_shapes_stagewise_and_fused(kw):
+    cfg = small_config(**kw)
+    _say(f"small shape {kw}")
+    w = make_workload(cfg, DEV)
+    rows = list(range(cfg.rows))
+    ref = oracle_rows(w, rows)
+    got = run_stages(w)
+    err = compare_rows(w, got, rows, ref)
+    fused = run_fused(w)
+    for k in ("selected", "page_table", "out"):
+        assert torch.equal(fused[k], got[k]), f"fused {k} differs from stage-wise"
+    check_invariants(w, fused)
+    _say(f"  max abs err {err:.3g} (tol {TOL[cfg.kv_dtype]})")
+
+
+def test_fused_without_exported_tables():
+    cfg = small_config(batch=3, query_len=2, ctx_lo=3000, ctx_hi=9000, seed=12)
+    w = make_workload(cfg, DEV)
+    a = run_fused(w, export=True)
+    b = run_fused(w, export=False)
+    assert torch.equal(a["out"], b["out"])
+
+
+def test_non_default_stream_and_determinism():
+    cfg = small_config(batch=4, query_len=2, ctx_lo=3000, ctx_hi=12000, num_q_heads=16,
+                       num_kv_heads=2, seed=13)
+    w = make_workload(cfg, DEV)
+    base = run_fused(w)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        again = run_fused(w, stream=s)
+    s.synchronize()
+    for k in ("selected", "page_table", "out"):
+        assert torch.equal(base[k], again[k])
+    for _ in range(5):
+        rep = run_fused(w)
+        assert torch.equal(rep["out"], base["out"])
+
+
+def test_dispatch_record_names_kernels():
+    cfg = small_config(batch=2, ctx_lo=3000, ctx_hi=5000, seed=14)
+    w = make_workload(cfg, DEV)
+    run_fused(w)
+    rec = msa.msa_last_dispatch()
+    for name in ("index_scan<bf16", "select_topk", "sparse_attn<bf16>"):
+        assert name in rec, rec
+
+
+def test_workspace_too_small_is_rejected():
+    cfg = small_config(batch=2, ctx_lo=3000, ctx_hi=5000, seed=15)
+    w = make_workload(cfg, DEV)
+    p = problem_for(w)
+    t = tensors_for(w)
+    need = msa.msa_workspace_bytes(p)
+    ws = torch.empty(need - 256, dtype=torch.uint8, device=DEV)
+    out = torch.empty((cfg.rows, cfg.num_q_heads, 128), dtype=torch.float32, device=DEV)
+    with pytest.raises(msa.MSAError) as ei:
+        msa.msa_decode(p, t, None, None, out, ws)
+    assert ei.value.status == msa.MSA_ERR_WORKSPACE
+
+
+# --------------------------------------------------------- full workloads
+SAMPLE_ROWS = {"tiny_4k": None, "tp8_rank_32k": 6, "layer_128k": 6, "spec_verify_fp8": 12,
+               "ctx_1m_nvfp4": 4}
+
+
+@pytest.mark.parametrize("name", CONFIG_ORDER)
+def test_full_workload_parity(name):
+    cfg = CONFIGS[name]
+    _say(f"full workload {name}: generating")
+    w = make_workload(cfg, DEV)
+    torch.cuda.synchronize()
+    _say(f"full workload {name}: running fused path")
+    got = run_fused(w)
+    stages = run_stages(w)
+    for k in ("selected", "page_table", "out"):
+        assert torch.equal(got[k], stages[k]), f"{name}: fused {k} differs from stage-wise"
+    got["scores"] = stages["scores"]
+    got["n_selected"] = stages["n_selected"]
+    check_invariants(w, got)
+    n = SAMPLE_ROWS[name]
+    if n is None:
+        rows = list(range(cfg.rows))
+    else:
+        rng = np.random.default_rng(cfg.seed)
+        rows = sorted(set(int(x) for x in rng.choice(cfg.rows, size=n, replace=False)) |
+                      {0, cfg.rows - 1})
+    _say(f"full workload {name}: oracle on rows {rows}")
+    err = compare_rows(w, got, rows)
+    # planted blocks are kept for every row 0 of a request
+    if cfg.n_plant and cfg.query_len == 1:
+        sel = got["selected"].cpu().numpy()
+        for b in range(cfg.batch):
+            if len(w.planted[b]) <= cfg.topk - 1:
+                assert set(w.planted[b]) <= set(sel[b].tolist()), f"request {b}"
+            else:
+                assert len(set(w.planted[b]) & set(sel[b].tolist())) == cfg.topk - 1
+    _say(f"full workload {name}: max abs err {err:.3g}")
+    del w, got, stages
+    torch.cuda.empty_cache()
