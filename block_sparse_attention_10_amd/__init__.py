@@ -6,7 +6,7 @@ library's HIP kernels.
 """
 from ._binding import (DTYPES, EXPORTS, MSA_ERR_HIP, MSA_ERR_INVALID_ARG,  # noqa: F401
                        MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE, MSA_OK, MSAError, Problem,
-                       Tensors, lib, library_path, msa_build_page_table, msa_decode,
+                       Tensors, describe, lib, library_path, msa_build_page_table, msa_decode,
                        msa_index_score, msa_last_dispatch, msa_last_hip_error,
                        msa_select_blocks, msa_selftest_decoders, msa_sparse_decode,
                        msa_status_string, msa_workspace_bytes, problem, tensors)

@@ -127,6 +127,25 @@ def tensors(q=None, idx_q=None, k_pool=None, v_pool=None, k_scale=None, v_scale=
                       ctx_lens)))
 
 
+def describe(q, idx_q, k_pool, v_pool, k_scale, v_scale, idx_k_pool, block_table, ctx_lens,
+             decode_query_len=1, topk=16, sm_scale=0.0):
+    """(Problem, Tensors) for device tensors in the boundary's layouts; the
+    dimensions and dtypes are read from the tensor shapes."""
+    B = int(ctx_lens.shape[0])
+    if k_pool.dtype == torch.bfloat16:
+        kv = "bf16"
+    elif k_scale is not None and k_scale.dtype == torch.float32:
+        kv = "fp8"
+    else:
+        kv = "nvfp4"
+    p = problem(B, decode_query_len, int(q.shape[1]), int(k_pool.shape[1]),
+                int(idx_k_pool.shape[1]), int(block_table.shape[1]), int(k_pool.shape[0]),
+                kv_dtype=kv, idx_k_dtype="bf16" if idx_k_pool.dtype == torch.bfloat16 else "fp8",
+                topk=topk, sm_scale=sm_scale)
+    t = tensors(q, idx_q, k_pool, v_pool, k_scale, v_scale, idx_k_pool, block_table, ctx_lens)
+    return p, t
+
+
 def _stream(stream):
     if stream is None:
         return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)

@@ -18,19 +18,19 @@ from tests.refs import problem_of
 TOL = {"bf16": 2e-3, "fp8": 1e-2, "nvfp4": 1e-2}
 
 
-def problem_for(w: Workload, **over):
-    c = w.cfg
-    kw = dict(topk=c.topk)
-    kw.update(over)
-    return msa.problem(c.batch, c.query_len, c.num_q_heads, c.num_kv_heads, c.num_idx_heads,
-                       c.max_blocks, w.num_phys_blocks, c.kv_dtype, c.idx_dtype, **kw)
+def problem_for(w: Workload):
+    return describe_workload(w)[0]
 
 
 def tensors_for(w: Workload):
+    return describe_workload(w)[1]
+
+
+def describe_workload(w: Workload):
     t = w.tensors
-    return msa.tensors(q=t["q"], idx_q=t["idx_q"], k_pool=t["k_pool"], v_pool=t["v_pool"],
-                       k_scale=t["k_scale"], v_scale=t["v_scale"], idx_k_pool=t["idx_k_pool"],
-                       block_table=t["block_table"], ctx_lens=t["ctx_lens"])
+    return msa.describe(t["q"], t["idx_q"], t["k_pool"], t["v_pool"], t["k_scale"], t["v_scale"],
+                        t["idx_k_pool"], t["block_table"], t["ctx_lens"],
+                        decode_query_len=w.cfg.query_len, topk=w.cfg.topk)
 
 
 def alloc_outputs(w: Workload, p):
