@@ -10,8 +10,9 @@
 // of the KV allocation, never a copy.
 //
 // Design (gfx950):
-//  * A workgroup of 4 waves owns one (row, KV head, split).  Each wave walks
-//    chunks of 32 keys (two 16-token pages) of the row's page table.
+//  * A workgroup of 4, 8 or 16 waves owns one (row, KV head, split).  Each
+//    wave walks chunks of 32 keys (two 16-token pages) of the row's page
+//    table; when a workgroup holds the whole row it writes the output itself.
 //  * QK^T on MFMA v_mfma_f32_16x16x32_bf16 with keys as the M dimension and
 //    the GQA group's query heads (up to 16) as N: S^T = K Q^T.  K rows go
 //    straight from HBM into the A operand (each lane 64 contiguous bytes of
@@ -26,7 +27,10 @@
 //    logit, the V scale multiplies P.  4-bit K/V: e2m1 x e4m3 -> bf16 is
 //    exact (at most 6 significant bits) and happens in registers.
 //  * Split partials (m, l, unnormalised O) combine inside the workgroup in
-//    LDS; across workgroups a small merge kernel applies the LSE rule.
+//    LDS; when a row is split over several workgroups a small merge kernel
+//    applies the log-sum-exp rule.  (Merging in the last workgroup to finish
+//    was measured slower on MI355X: the cross-workgroup hand-off stalls every
+//    workgroup on a write-through store and a returning atomic.)
 #include "msa_device.h"
 #include "msa_internal.h"
 
@@ -58,37 +62,50 @@ struct Chunk {
   f32x4 kscale, vscale;  // fp8: per-token scales of this lane's 4 S^T rows
 };
 
+// First head dim of the 8-dim slice that lane group g (= lane / 16) feeds
+// into K-step kk of the QK^T MFMA.  The contraction order is free as long as
+// K and Q agree; each dtype picks the order that makes its K loads cover
+// contiguous runs of a key row.
+template <int KV>
+__device__ __forceinline__ int kdim(int g, int kk) {
+  if constexpr (KV == 0) return 32 * kk + 8 * g;                         // 64 B per row per load
+  else if constexpr (KV == 1) return 64 * (kk >> 1) + 16 * g + 8 * (kk & 1);  // 64 B per row
+  else return 32 * g + 8 * kk;                                            // whole 64 B row
+}
+
+// Loads of one 16-token page.  K: lane (key m = lane % 16, group g) holds the
+// slices kdim(g, .) of key m.  V: each load instruction covers a contiguous
+// 1 KB run of the page (bf16, fp8) or the whole page (4-bit).
 template <int KV>
 __device__ __forceinline__ void load_page(Chunk<KV>& c, const uint8_t* __restrict__ k_pool,
                                           const uint8_t* __restrict__ v_pool,
                                           const void* __restrict__ k_scale,
                                           const void* __restrict__ v_scale, size_t row0,
                                           int lane) {
-  const int kr = lane & 15, kg = lane >> 4;  // K: key row, 32-dim group
-  const int vr = lane >> 2, vg = lane & 3;   // V: key row, 32-dim group
+  const int m = lane & 15, g = lane >> 4;
   if constexpr (KV == 0) {
-    const uint8_t* kp = k_pool + (row0 + kr) * 256 + kg * 64;
-    const uint8_t* vp = v_pool + (row0 + vr) * 256 + vg * 64;
+    const uint8_t* kp = k_pool + (row0 + m) * 256 + 16 * g;
+    const uint8_t* vp = v_pool + row0 * 256 + 16 * lane;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) c.k[i] = ldg128(kp + 16 * i);
+    for (int i = 0; i < 4; ++i) c.k[i] = ldg128_stream(kp + 64 * i);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) c.v[i] = ldg128(vp + 16 * i);
+    for (int i = 0; i < 4; ++i) c.v[i] = ldg128_stream(vp + 1024 * i);
   } else if constexpr (KV == 1) {
-    const uint8_t* kp = k_pool + (row0 + kr) * 128 + kg * 32;
-    const uint8_t* vp = v_pool + (row0 + vr) * 128 + vg * 32;
-    c.k[0] = ldg128(kp);
-    c.k[1] = ldg128(kp + 16);
-    c.v[0] = ldg128(vp);
-    c.v[1] = ldg128(vp + 16);
-    c.kscale = *reinterpret_cast<const f32x4*>(static_cast<const float*>(k_scale) + row0 + 4 * kg);
-    c.vscale = *reinterpret_cast<const f32x4*>(static_cast<const float*>(v_scale) + row0 + 4 * kg);
+    const uint8_t* kp = k_pool + (row0 + m) * 128 + 16 * g;
+    const uint8_t* vp = v_pool + row0 * 128 + 16 * lane;
+    c.k[0] = ldg128_stream(kp);
+    c.k[1] = ldg128_stream(kp + 64);
+    c.v[0] = ldg128_stream(vp);
+    c.v[1] = ldg128_stream(vp + 1024);
+    c.kscale = *reinterpret_cast<const f32x4*>(static_cast<const float*>(k_scale) + row0 + 4 * g);
+    c.vscale = *reinterpret_cast<const f32x4*>(static_cast<const float*>(v_scale) + row0 + 4 * g);
   } else {
-    c.k[0] = ldg128(k_pool + (row0 + kr) * 64 + kg * 16);
-    c.v[0] = ldg128(v_pool + (row0 + vr) * 64 + vg * 16);
+    c.k[0] = ldg128_stream(k_pool + (row0 + m) * 64 + 16 * g);
+    c.v[0] = ldg128_stream(v_pool + row0 * 64 + 16 * lane);
     c.ks = *reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(k_scale) +
-                                              (row0 + kr) * 8 + kg * 2);
+                                              (row0 + m) * 8 + 2 * g);
     c.vs = *reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(v_scale) +
-                                              (row0 + vr) * 8 + vg * 2);
+                                              (row0 + (lane >> 2)) * 8 + 2 * (lane & 3));
   }
 }
 
@@ -101,7 +118,7 @@ __device__ __forceinline__ void e2m1x8_to_bf16(uint32_t w, float s, uint32_t* ou
   }
 }
 
-// A operand (16 keys x 8 dims) of K-step kk for this lane, as bf16.
+// A operand (16 keys x 8 dims, dims kdim(g, kk)) of K-step kk, as bf16.
 template <int KV>
 __device__ __forceinline__ bf16x8 k_operand(const Chunk<KV>& c, int kk) {
   if constexpr (KV == 0) {
@@ -127,42 +144,61 @@ __device__ __forceinline__ bf16x8 k_operand(const Chunk<KV>& c, int kk) {
   }
 }
 
-// This lane's 32 V values of its key row, as 16 packed bf16 dwords.
+__device__ __forceinline__ void lds_write16(uint8_t* dst, uint32_t a, uint32_t b, uint32_t c,
+                                            uint32_t d) {
+  *reinterpret_cast<uint2*>(dst) = make_uint2(a, b);
+  *reinterpret_cast<uint2*>(dst + 8) = make_uint2(c, d);
+}
+
+// Write this lane's share of one V page into the page's 16 LDS rows (bf16,
+// kVRow bytes apart), converting fp8 / e2m1 to bf16 on the way.
 template <int KV>
-__device__ __forceinline__ void v_bf16(const Chunk<KV>& c, uint32_t* o) {
+__device__ __forceinline__ void stage_v(const Chunk<KV>& c, uint8_t* page_rows, int lane) {
   if constexpr (KV == 0) {
+    // load i: key 4i + lane/16, dims 8*(lane%16)..+8
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      o[4 * i] = c.v[i].x; o[4 * i + 1] = c.v[i].y; o[4 * i + 2] = c.v[i].z; o[4 * i + 3] = c.v[i].w;
-    }
+    for (int i = 0; i < 4; ++i)
+      lds_write16(page_rows + (4 * i + (lane >> 4)) * kVRow + 16 * (lane & 15), c.v[i].x,
+                  c.v[i].y, c.v[i].z, c.v[i].w);
   } else if constexpr (KV == 1) {
+    // load i: key 8i + lane/8, dims 16*(lane%8)..+16
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const uint32_t src[4] = {c.v[i].x, c.v[i].y, c.v[i].z, c.v[i].w};
+      uint32_t o[8];
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        o[8 * i + 2 * w] = e4m3x2_to_bf16x2<false>(src[w]);
-        o[8 * i + 2 * w + 1] = e4m3x2_to_bf16x2<true>(src[w]);
+        o[2 * w] = e4m3x2_to_bf16x2<false>(src[w]);
+        o[2 * w + 1] = e4m3x2_to_bf16x2<true>(src[w]);
       }
+      uint8_t* dst = page_rows + (8 * i + (lane >> 3)) * kVRow + 32 * (lane & 7);
+      lds_write16(dst, o[0], o[1], o[2], o[3]);
+      lds_write16(dst + 16, o[4], o[5], o[6], o[7]);
     }
   } else {
+    // key lane/4, dims 32*(lane%4)..+32
     const uint32_t src[4] = {c.v[0].x, c.v[0].y, c.v[0].z, c.v[0].w};
     const float s0 = e4m3_to_f32(c.vs & 0xFFu);
     const float s1 = e4m3_to_f32((c.vs >> 8) & 0xFFu);
+    uint8_t* dst = page_rows + (lane >> 2) * kVRow + 64 * (lane & 3);
 #pragma unroll
-    for (int w = 0; w < 4; ++w) e2m1x8_to_bf16(src[w], w < 2 ? s0 : s1, o + 4 * w);
+    for (int w = 0; w < 4; ++w) {
+      uint32_t o[4];
+      e2m1x8_to_bf16(src[w], w < 2 ? s0 : s1, o);
+      lds_write16(dst + 16 * w, o[0], o[1], o[2], o[3]);
+    }
   }
 }
 
-template <int KV>
-__global__ __launch_bounds__(256, 2) void sparse_attn_kernel(
+template <int KV, int W>
+__global__ __launch_bounds__(64 * W, 4) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ k_pool,
     const uint8_t* __restrict__ v_pool, const void* __restrict__ k_scale,
     const void* __restrict__ v_scale, const int32_t* __restrict__ page_table,
     const int32_t* __restrict__ ctx_lens, float* __restrict__ part_o,
-    float* __restrict__ part_ml, float* __restrict__ out, int T, int Hq, int Hkv, int PT,
-    int S, int cpw, float scale_log2) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * kStage];
+    float* __restrict__ part_ml, float* __restrict__ out, int T, int Hq, int Hkv, int PT, int S,
+    int cpw, int max_page, float scale_log2) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[W * kStage];
 
   const int lane = lane_id();
   const int wave = wave_id();
@@ -178,8 +214,9 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(
 
   // valid pages of the row (the table is -1 padded at the end)
   const int32_t* prow = page_table + (size_t)r * PT;
-  int nvp = __popcll(__ballot(lane < PT && prow[lane] >= 0));
-  if (PT > kWave) nvp += __popcll(__ballot(lane + kWave < PT && prow[lane + kWave] >= 0));
+  const int pt_lo = lane < PT ? prow[lane] : -1;
+  const int pt_hi = lane + kWave < PT ? prow[lane + kWave] : -1;
+  const int nvp = __popcll(__ballot(pt_lo >= 0)) + __popcll(__ballot(pt_hi >= 0));
   const int nblk = nvp >> 3;
   const int kv_len = nblk > 0 ? 128 * (nblk - 1) + (pos & 127) + 1 : 0;
 
@@ -189,10 +226,10 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(
   bf16x8 qop[4];
   {
     u32x4 z = {0u, 0u, 0u, 0u};
-    const uint16_t* qp = q + ((size_t)r * Hq + g * G + min(hl, G - 1)) * kD + 32 * g4;
+    const uint16_t* qp = q + ((size_t)r * Hq + g * G + min(hl, G - 1)) * kD;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      u32x4 v = ldg128(qp + 8 * kk);
+      u32x4 v = ldg128(qp + kdim<KV>(g4, kk));
       qop[kk] = __builtin_bit_cast(bf16x8, hl < G ? v : z);
     }
   }
@@ -205,25 +242,21 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(
   uint8_t* stage = smem + wave * kStage;
   const size_t kv_head_rows = 128;
   for (int k = 0; k < cpw; ++k) {
-    const int ci = split * 4 * cpw + wave + 4 * k;
+    const int ci = split * W * cpw + wave + W * k;
     if (ci * kChunk >= kv_len) break;
     Chunk<KV> ch[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int P = __builtin_amdgcn_readfirstlane(prow[2 * ci + j]);
+      const int idx = 2 * ci + j;  // wave-uniform
+      int P = idx < kWave ? __builtin_amdgcn_readlane(pt_lo, idx)
+                          : __builtin_amdgcn_readlane(pt_hi, idx - kWave);
+      P = min(max(P, 0), max_page);  // a malformed table cannot reach outside the pools
       const size_t row0 = ((size_t)(P >> 3) * Hkv + g) * kv_head_rows + (size_t)(P & 7) * 16;
       load_page<KV>(ch[j], k_pool, v_pool, k_scale, v_scale, row0, lane);
     }
-    // stage V rows into LDS: lane writes 64 B of key row 16*j + lane/4
+    // stage the two V pages into LDS rows 0..15 and 16..31
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      uint32_t vb[16];
-      v_bf16<KV>(ch[j], vb);
-      uint8_t* dst = stage + (16 * j + (lane >> 2)) * kVRow + (lane & 3) * 64;
-#pragma unroll
-      for (int w = 0; w < 8; ++w)
-        *reinterpret_cast<uint2*>(dst + 8 * w) = make_uint2(vb[2 * w], vb[2 * w + 1]);
-    }
+    for (int j = 0; j < 2; ++j) stage_v<KV>(ch[j], stage + 16 * j * kVRow, lane);
     // S^T = K Q^T for the two pages
     f32x4 sacc[2];
 #pragma unroll
@@ -301,11 +334,11 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
 
-  // combine the four waves in LDS
+  // combine the W waves in LDS
   __syncthreads();
-  float* m_w = reinterpret_cast<float*>(smem);  // [4][16]
-  float* l_w = m_w + 64;                        // [4][16]
-  float* o_w = l_w + 64;                        // [4][16][kORow]
+  float* m_w = reinterpret_cast<float*>(smem);  // [W][16]
+  float* l_w = m_w + 16 * W;                    // [W][16]
+  float* o_w = l_w + 16 * W;                    // [W][16][kORow]
   if (lane < 16) {
     m_w[wave * 16 + lane] = m;
     l_w[wave * 16 + lane] = lsum;
@@ -315,15 +348,15 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) o_w[(wave * 16 + hl) * kORow + 16 * s + 4 * g4 + i] = oacc[s][i];
   __syncthreads();
-  for (int idx = threadIdx.x; idx < G * kD; idx += 256) {
+  for (int idx = threadIdx.x; idx < G * kD; idx += 64 * W) {
     const int h = idx >> 7;
     const int d = idx & (kD - 1);
     float M = neg_inf();
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, m_w[w * 16 + h]);
+    for (int w = 0; w < W; ++w) M = fmaxf(M, m_w[w * 16 + h]);
     float O = 0.f, Ls = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < W; ++w) {
       const float mw = m_w[w * 16 + h];
       const float f = mw == neg_inf() ? 0.f : __builtin_amdgcn_exp2f(mw - M);
       O += f * o_w[(w * 16 + h) * kORow + d];
@@ -375,31 +408,51 @@ __global__ void selftest_kernel(float* out) {
   }
 }
 
+template <int KV, int W>
+hipError_t launch_kvw(const Dims& d, const SplitPlan& sp, const void* q, const void* k_pool,
+                      const void* v_pool, const void* k_scale, const void* v_scale,
+                      const int32_t* page_table, const int32_t* ctx_lens, float* part_o,
+                      float* part_ml, float* out, hipStream_t s) {
+  const long wgs = (long)d.R() * d.Hkv * sp.splits;
+  hipLaunchKernelGGL((sparse_attn_kernel<KV, W>), dim3((unsigned)wgs), dim3(64 * W), 0, s,
+                     static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(k_pool),
+                     static_cast<const uint8_t*>(v_pool), k_scale, v_scale, page_table,
+                     ctx_lens, part_o, part_ml, out, d.T, d.Hq, d.Hkv, d.PT(), sp.splits,
+                     sp.cpw, d.NB * 8 - 1, d.scale_log2);
+  return hipGetLastError();
+}
+
 template <int KV>
 hipError_t launch_kv(const Dims& d, const SplitPlan& sp, const void* q, const void* k_pool,
                      const void* v_pool, const void* k_scale, const void* v_scale,
                      const int32_t* page_table, const int32_t* ctx_lens, float* part_o,
                      float* part_ml, float* out, hipStream_t s) {
-  const long wgs = (long)d.R() * d.Hkv * sp.splits;
-  hipLaunchKernelGGL((sparse_attn_kernel<KV>), dim3((unsigned)wgs), dim3(256), 0, s,
-                     static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(k_pool),
-                     static_cast<const uint8_t*>(v_pool), k_scale, v_scale, page_table,
-                     ctx_lens, part_o, part_ml, out, d.T, d.Hq, d.Hkv, d.PT(), sp.splits,
-                     sp.cpw, d.scale_log2);
-  return hipGetLastError();
+  if (sp.waves == 16)
+    return launch_kvw<KV, 16>(d, sp, q, k_pool, v_pool, k_scale, v_scale, page_table, ctx_lens,
+                              part_o, part_ml, out, s);
+  if (sp.waves == 8)
+    return launch_kvw<KV, 8>(d, sp, q, k_pool, v_pool, k_scale, v_scale, page_table, ctx_lens,
+                             part_o, part_ml, out, s);
+  return launch_kvw<KV, 4>(d, sp, q, k_pool, v_pool, k_scale, v_scale, page_table, ctx_lens,
+                           part_o, part_ml, out, s);
 }
 
 }  // namespace
 
 SplitPlan plan_splits(const Dims& d) {
-  // Aim at ~4096 waves (16 per CU) while keeping split partials small.
+  // At least one workgroup per CU (256), split a row's chunks only as far as
+  // needed, and keep >= 4 chunks per split; waves per workgroup follow the
+  // chunks a split holds.  The 128K layer (256 row x KV-head pairs) gets one
+  // 16-wave workgroup per pair and no merge pass.
   const int chunks = d.PT() / 2;
   const long pairs = (long)d.R() * d.Hkv;
-  int cpw = 1;
-  while (cpw < chunks / 4 && pairs * 4 * ((chunks + 4 * cpw - 1) / (4 * cpw)) > 4096) cpw *= 2;
+  int S = 1;
+  while (S * 2 <= chunks / 4 && pairs * S < 256) S *= 2;
+  const int per_split = (chunks + S - 1) / S;
   SplitPlan p;
-  p.cpw = cpw;
-  p.splits = (chunks + 4 * cpw - 1) / (4 * cpw);
+  p.splits = S;
+  p.waves = per_split >= 16 ? 16 : (per_split >= 8 ? 8 : 4);
+  p.cpw = (per_split + p.waves - 1) / p.waves;
   return p;
 }
 
@@ -423,8 +476,9 @@ hipError_t launch_sparse_attention(const Dims& d, const void* q, const void* k_p
   static const char* names[3] = {"bf16", "fp8", "nvfp4"};
   if (note)
     *note += std::string("sparse_attn<") + names[d.kv_dtype] + ">[grid=" +
-             std::to_string((long)d.R() * d.Hkv * sp.splits) + "x256,splits=" +
-             std::to_string(sp.splits) + ",chunks_per_wave=" + std::to_string(sp.cpw) + "]";
+             std::to_string((long)d.R() * d.Hkv * sp.splits) + "x" + std::to_string(64 * sp.waves) +
+             ",splits=" + std::to_string(sp.splits) + ",chunks_per_wave=" +
+             std::to_string(sp.cpw) + "]";
   if (sp.splits > 1) {
     const unsigned rows = (unsigned)((long)d.R() * d.Hq);
     hipLaunchKernelGGL(lse_merge_kernel, dim3(rows), dim3(kD), 0, s, part_o, part_ml, out,

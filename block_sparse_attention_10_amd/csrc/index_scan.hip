@@ -40,13 +40,15 @@ __device__ __forceinline__ void fold_stage(float* v, int lane) {
   }
 }
 
-// KB: bytes per key element (2 = bf16, 1 = fp8 e4m3).  TR: rows scored per
-// pass (1, 2 or 4); more rows loop over passes.
+// Scores of logical block c (a real block: c * 128 < L) for every row of
+// request b, written by lane 0.  KB: bytes per key element (2 = bf16, 1 =
+// fp8 e4m3).  TR: rows scored per pass (1, 2 or 4); more rows loop.
 template <int KB, int TR>
-__global__ __launch_bounds__(256) void index_scan_kernel(
-    const uint16_t* __restrict__ idx_q, const uint8_t* __restrict__ idx_k,
-    const int32_t* __restrict__ block_table, const int32_t* __restrict__ ctx_lens,
-    float* __restrict__ scores, int B, int T, int Hidx, int MAXB) {
+__device__ __forceinline__ void scan_block(const uint16_t* __restrict__ idx_q,
+                                           const uint8_t* __restrict__ idx_k,
+                                           const int32_t* __restrict__ block_table,
+                                           float* __restrict__ scores, int b, int c, int L, int T,
+                                           int Hidx, int MAXB, int lane) {
   constexpr int DPL = 16 / KB;       // dims per lane per load (8 / 16)
   constexpr int LPT = kIdxDim / DPL; // lanes per token (8 / 4)
   constexpr int TPL = kWave / LPT;   // tokens per load instruction (8 / 16)
@@ -54,17 +56,7 @@ __global__ __launch_bounds__(256) void index_scan_kernel(
   constexpr int QW = DPL / 2;        // query dwords per lane per row (4 / 8)
   static_assert(NLD == 2 * LPT, "transpose-reduce leaves two tokens per lane");
 
-  const int lane = lane_id();
-  const int item = blockIdx.x * 4 + wave_id();
-  if (item >= B * MAXB) return;
-  const int b = item / MAXB;
-  const int c = item - b * MAXB;
-  const int L = ctx_lens[b];
   float* srow = scores + (size_t)b * T * MAXB + c;
-  if (c * kBlock > L - 1) {  // past the last token: -inf for every row
-    for (int t = lane; t < T; t += kWave) srow[(size_t)t * MAXB] = -INFINITY;
-    return;
-  }
   const size_t head_bytes = (size_t)kBlock * kIdxDim * KB;
   const uint8_t* kblk =
       idx_k + (size_t)block_table[(size_t)b * MAXB + c] * Hidx * head_bytes + lane * 16;
@@ -81,7 +73,7 @@ __global__ __launch_bounds__(256) void index_scan_kernel(
       u32x4 kv[NLD];
       const uint8_t* kh = kblk + (size_t)h * head_bytes;
 #pragma unroll
-      for (int i = 0; i < NLD; ++i) kv[i] = ldg128(kh + i * 1024);
+      for (int i = 0; i < NLD; ++i) kv[i] = ldg128_stream(kh + i * 1024);
       uint32_t qv[TR][QW];
 #pragma unroll
       for (int t = 0; t < TR; ++t) {
@@ -142,28 +134,44 @@ __global__ __launch_bounds__(256) void index_scan_kernel(
   }
 }
 
+// msa_index_score: one wave per (request, logical block); blocks past the
+// context score -inf for every row.
+template <int KB, int TR>
+__global__ __launch_bounds__(256) void index_scan_kernel(
+    const uint16_t* __restrict__ idx_q, const uint8_t* __restrict__ idx_k,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ ctx_lens,
+    float* __restrict__ scores, int B, int T, int Hidx, int MAXB) {
+  const int lane = lane_id();
+  const int item = blockIdx.x * 4 + wave_id();
+  if (item >= B * MAXB) return;
+  const int b = item / MAXB;
+  const int c = item - b * MAXB;
+  const int L = ctx_lens[b];
+  if (c * kBlock > L - 1) {
+    float* srow = scores + (size_t)b * T * MAXB + c;
+    for (int t = lane; t < T; t += kWave) srow[(size_t)t * MAXB] = -INFINITY;
+    return;
+  }
+  scan_block<KB, TR>(idx_q, idx_k, block_table, scores, b, c, L, T, Hidx, MAXB, lane);
+}
+
 template <int KB>
-hipError_t launch_kb(const Dims& d, const void* idx_q, const void* idx_k,
-                     const int32_t* bt, const int32_t* cl, float* scores, hipStream_t s,
-                     std::string* note) {
+hipError_t launch_kb(const Dims& d, const void* idx_q, const void* idx_k, const int32_t* bt,
+                     const int32_t* cl, float* scores, hipStream_t s, std::string* note) {
   const long items = (long)d.B * d.MAXB;
   const dim3 grid((unsigned)((items + 3) / 4)), block(256);
   const auto* q = static_cast<const uint16_t*>(idx_q);
   const auto* k = static_cast<const uint8_t*>(idx_k);
-  int tr;
-  if (d.T == 1) {
-    tr = 1;
+  const int tr = d.T == 1 ? 1 : (d.T == 2 ? 2 : 4);
+  if (tr == 1)
     hipLaunchKernelGGL((index_scan_kernel<KB, 1>), grid, block, 0, s, q, k, bt, cl, scores, d.B,
                        d.T, d.Hidx, d.MAXB);
-  } else if (d.T == 2) {
-    tr = 2;
+  else if (tr == 2)
     hipLaunchKernelGGL((index_scan_kernel<KB, 2>), grid, block, 0, s, q, k, bt, cl, scores, d.B,
                        d.T, d.Hidx, d.MAXB);
-  } else {
-    tr = 4;
+  else
     hipLaunchKernelGGL((index_scan_kernel<KB, 4>), grid, block, 0, s, q, k, bt, cl, scores, d.B,
                        d.T, d.Hidx, d.MAXB);
-  }
   if (note)
     *note += std::string("index_scan<") + (KB == 2 ? "bf16" : "fp8") + ",rows" +
              std::to_string(tr) + ">[grid=" + std::to_string(grid.x) + "x256]";

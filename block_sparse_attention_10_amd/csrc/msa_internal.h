@@ -21,10 +21,11 @@ struct Dims {
   int PT() const { return topk * 8; }  // page-table row length
 };
 
-// Attention split plan: a workgroup of 4 waves covers 4 * cpw chunks of 32
-// keys (two 16-token pages) of one (row, KV head); `splits` workgroups per
-// (row, KV head) together cover the row's page table.
+// Attention split plan: a workgroup of `waves` waves covers waves * cpw
+// chunks of 32 keys (two 16-token pages) of one (row, KV head); `splits`
+// workgroups per (row, KV head) together cover the row's page table.
 struct SplitPlan {
+  int waves;   // waves per workgroup: 4, 8 or 16
   int cpw;     // chunks per wave
   int splits;  // workgroups per (row, KV head)
 };
@@ -47,6 +48,8 @@ hipError_t launch_select(const Dims& d, const float* scores, const int32_t* ctx_
 hipError_t launch_page_table(const Dims& d, const int32_t* selected, const int32_t* block_table,
                              int32_t* page_table, hipStream_t s, std::string* note);
 
+// One launch when a workgroup covers a whole (row, KV head); otherwise the
+// split partials land in part_o / part_ml and a merge launch follows.
 hipError_t launch_sparse_attention(const Dims& d, const void* q, const void* k_pool,
                                    const void* v_pool, const void* k_scale,
                                    const void* v_scale, const int32_t* page_table,

@@ -15,143 +15,25 @@
 // candidates in ascending id order into a register-resident sorted list of
 // the topk - 1 best 64-bit keys (orderable score << 32 | ~id, so a larger
 // key is a better block and equal scores favour the lower id).  The wave
-// then pops its topk - 1 best keys by repeated wave maxima, the waves of a
-// row meet in LDS, and one wave ranks the union, sorts the winners by id and
+// then pops its topk - 1 best keys by repeated wave maxima (DPP reductions,
+// no LDS traffic), the waves of a row meet in LDS, and one wave ranks the
+// union (at most 60 finalists, one per lane), sorts the winners by id and
 // writes the row's selection and page table.
 #include "msa_device.h"
 #include "msa_internal.h"
+#include "select_device.h"
 
 namespace msa {
 namespace {
-
-constexpr int kMaxTopk = 16;
-constexpr int kList = kMaxTopk - 1;  // per-lane list length (non-local picks)
-
-// Monotone map fp32 -> uint32 for a total order; NaN ranks as -inf and -0
-// as +0.
-__device__ __forceinline__ uint32_t orderable(float s) {
-  if (s != s) s = -INFINITY;
-  if (s == 0.f) s = 0.f;
-  const uint32_t u = __builtin_bit_cast(uint32_t, s);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ __forceinline__ uint64_t make_key(float s, int c) {
-  return ((uint64_t)orderable(s) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)c);
-}
-
-__device__ __forceinline__ int key_id(uint64_t k) {
-  return (int)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFu));
-}
 
 __global__ __launch_bounds__(256) void select_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ ctx_lens,
     const int32_t* __restrict__ block_table, int32_t* __restrict__ selected,
     int32_t* __restrict__ n_selected, int32_t* __restrict__ page_table, int T, int MAXB,
     int topk) {
-  __shared__ uint64_t wave_best[4][kList];
-  __shared__ int32_t row_sel[4][kMaxTopk];
-
-  const int lane = lane_id();
-  const int wave = wave_id();
-  const int b = blockIdx.x;
-  const int L = ctx_lens[b];
-  const int parts = T >= 4 ? 1 : (T == 1 ? 4 : (T == 2 ? 2 : 1));
-  const int rows_per_pass = 4 / parts;
-  const int K1 = topk - 1;
-
-  for (int t0 = 0; t0 < T; t0 += rows_per_pass) {
-    const int t = t0 + wave / parts;
-    const int part = wave % parts;
-    const bool active = t < T;
-    const int pos = L - T + t;
-    const int local = pos >> 7;
-    const bool take_all = local + 1 <= topk;
-    const int r = b * T + t;
-
-    if (active && !take_all && K1 > 0) {
-      const float* srow = scores + (size_t)r * MAXB;
-      uint64_t list[kList];
-#pragma unroll
-      for (int j = 0; j < kList; ++j) list[j] = 0;  // 0 ranks below every real key
-      for (int c = part * kWave + lane; c < local; c += parts * kWave) {
-        uint64_t x = make_key(srow[c], c);
-        if (x > list[kList - 1]) {
-#pragma unroll
-          for (int j = 0; j < kList; ++j) {
-            const uint64_t y = list[j];
-            const bool gt = x > y;
-            list[j] = gt ? x : y;
-            x = gt ? y : x;
-          }
-        }
-      }
-      for (int k = 0; k < K1; ++k) {
-        const uint64_t best = wave_max_u64(list[0]);
-        if (lane == 0) wave_best[wave][k] = best;
-        if (best != 0 && list[0] == best) {
-#pragma unroll
-          for (int j = 0; j < kList - 1; ++j) list[j] = list[j + 1];
-          list[kList - 1] = 0;
-        }
-      }
-    }
-    __syncthreads();
-
-    if (active && part == 0) {
-      int n = 0;
-      if (take_all) {
-        n = local + 1;
-        for (int k = lane; k < n; k += kWave) row_sel[wave][k] = k;
-      } else if (K1 == 0) {
-        if (lane == 0) row_sel[wave][0] = local;
-        n = 1;
-      } else {
-        // rank the union of this row's per-wave lists; keys are unique
-        const int m = parts * K1;
-        uint64_t mine = 0;
-        if (lane < m) mine = wave_best[wave + lane / K1][lane % K1];
-        int rank = 0;
-        for (int e = 0; e < m; ++e) {
-          const uint64_t o = wave_best[wave + e / K1][e % K1];
-          rank += o > mine ? 1 : 0;
-        }
-        const bool win = lane < m && rank < K1 && mine != 0;
-        const int id = key_id(mine);
-        // position among the winners by ascending id
-        __builtin_amdgcn_wave_barrier();
-        if (win) row_sel[wave][rank] = id;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        int posn = 0;
-        if (win)
-          for (int e = 0; e < K1; ++e) posn += row_sel[wave][e] < id ? 1 : 0;
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if (win) row_sel[wave][posn] = id;
-        if (lane == 0) row_sel[wave][K1] = local;
-        n = topk;
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      if (selected)
-        for (int k = lane; k < topk; k += kWave)
-          selected[(size_t)r * topk + k] = k < n ? row_sel[wave][k] : -1;
-      if (lane == 0 && n_selected) n_selected[r] = n;
-      if (page_table) {
-        const int pt = topk * 8;
-        for (int e = lane; e < pt; e += kWave) {
-          const int k = e >> 3;
-          int v = -1;
-          if (k < n) v = block_table[(size_t)b * MAXB + row_sel[wave][k]] * 8 + (e & 7);
-          page_table[(size_t)r * pt + e] = v;
-        }
-      }
-    }
-    __syncthreads();
-  }
+  __shared__ SelectLds sh;
+  select_request(blockIdx.x, scores, ctx_lens, block_table, selected, n_selected, page_table,
+                 T, MAXB, topk, sh);
 }
 
 __global__ __launch_bounds__(256) void page_table_kernel(const int32_t* __restrict__ selected,

@@ -156,11 +156,14 @@ int msa_build_page_table(const msa_problem* p, const int32_t* selected,
  * n < 128 * (blocks - 1) + (p mod 128) + 1.  out = softmax(q K^T * scale) V
  * per query head, computed split-K with fp32 partials in `workspace` and
  * merged by log-sum-exp.  Reads t->q, t->k_pool, t->v_pool, t->k_scale,
- * t->v_scale, t->ctx_lens.  Two launches. */
+ * t->v_scale, t->ctx_lens.  Page ids are clamped to the pools.  One launch,
+ * plus a merge launch when a row is split over several workgroups. */
 int msa_sparse_decode(const msa_problem* p, const msa_tensors* t, const int32_t* page_table,
                       float* out, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Steps 1-4 in one call.  selected / page_table may be NULL; when given they
+/* Steps 1-4 in one call: the index scan, the selection with the page table
+ * built in the same launch, then the attention (and its merge launch when
+ * rows are split).  selected / page_table may be NULL; when given they
  * receive the step 2 / step 3 results.  Block scores, counts and any table
  * not supplied live in `workspace`. */
 int msa_decode(const msa_problem* p, const msa_tensors* t, int32_t* selected,

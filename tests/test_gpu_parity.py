@@ -105,6 +105,40 @@ def test_dispatch_record_names_kernels():
     rec = msa.msa_last_dispatch()
     for name in ("index_scan<bf16", "select_topk", "sparse_attn<bf16>"):
         assert name in rec, rec
+    p = problem_for(w)
+    t = tensors_for(w)
+    scores = torch.empty((cfg.rows, cfg.max_blocks), dtype=torch.float32, device=DEV)
+    msa.msa_index_score(p, t, scores)
+    assert msa.msa_last_dispatch().startswith("index_scan<bf16")
+
+
+@pytest.mark.parametrize("kw", [
+    dict(batch=3, query_len=2, ctx_lo=3000, ctx_hi=9000, seed=16),
+    dict(batch=1, query_len=1, ctx_list=(70000,), num_q_heads=16, num_kv_heads=4,
+         num_idx_heads=2, seed=17),
+])
+def test_workspace_reuse_across_calls_and_entry_points(kw):
+    """One workspace, never cleared, serves many calls, alternating the fused
+    and the stage-wise attention entry points."""
+    cfg = small_config(**kw)
+    w = make_workload(cfg, DEV)
+    ref = run_stages(w)
+    p = problem_for(w)
+    t = tensors_for(w)
+    ws = torch.full((msa.msa_workspace_bytes(p),), 0xA5, dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(ref["out"])
+    sel = torch.empty_like(ref["selected"])
+    pt = torch.empty_like(ref["page_table"])
+    for i in range(6):
+        out.zero_()
+        if i % 2 == 0:
+            msa.msa_decode(p, t, sel, pt, out, ws)
+        else:
+            msa.msa_sparse_decode(p, t, ref["page_table"], out, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref["out"]), f"call {i}"
+        if i % 2 == 0:
+            assert torch.equal(sel, ref["selected"]) and torch.equal(pt, ref["page_table"])
 
 
 def test_workspace_too_small_is_rejected():
