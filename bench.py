@@ -24,7 +24,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
 METRIC = "MSA decode query-tokens/s at 128K ctx; achieved HBM GB/s vs peak"
-SCAN_KERNEL_SRC = os.path.join(ROOT, "block_sparse_attention_10_amd", "csrc", "index_scan.hip")
+SCAN_KERNEL_SRCS = [os.path.join(ROOT, "block_sparse_attention_10_amd", "csrc", f)
+                    for f in ("index_scan.hip", "msa_device.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "index_scan_layer_128k_traffic.json")
 
 
@@ -65,17 +66,20 @@ def algorithmic_bytes(w, selected):
     return {"index": idx, "kv": int(kv), "meta": int(meta), "total": int(idx + kv + meta)}
 
 
-def source_hash(path):
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+def source_hash(paths):
+    h = hashlib.sha256()
+    for path in paths:
+        h.update(open(path, "rb").read())
+    return h.hexdigest()[:16]
 
 
-def measured_traffic(launch_bytes):
+def measured_traffic():
     """HBM bytes per scan launch from committed rocprofv3 counter runs, if
     they were taken on the current scan kernel source."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     rec = json.load(open(TRAFFIC_FILE))
-    if rec.get("kernel_source_sha256_16") != source_hash(SCAN_KERNEL_SRC):
+    if rec.get("kernel_source_sha256_16") != source_hash(SCAN_KERNEL_SRCS):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -144,9 +148,15 @@ def main():
     ap.add_argument("--cpu-requests", type=int, default=32,
                     help="requests the CPU oracle baseline runs on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--calib-copy-mib", type=int, default=0,
-                    help="only run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--export-spec", default=None,
+                    help="write the workload's shapes, contexts and block table for the "
+                         "counter driver (block_sparse_attention_10_amd/driver) and exit")
     args = ap.parse_args()
+
+    if args.export_spec:
+        from synth import CONFIGS, write_spec
+        write_spec(CONFIGS[args.workload], args.export_spec)
+        return
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported by this build "
@@ -155,16 +165,6 @@ def main():
         sys.exit(2)
 
     import torch
-
-    if args.calib_copy_mib:
-        n = args.calib_copy_mib << 20
-        a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
-        b = torch.empty_like(a)
-        for _ in range(5):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        print(json.dumps({"calib_copy_bytes": n, "launches": 5}))
-        return
 
     import block_sparse_attention_10_amd as msa
     from synth import CONFIGS, make_workload
@@ -252,7 +252,7 @@ def main():
             "frac": achieved / PEAK_HBM_GBS,
             "avg_launch_us": scan_us,
             "algorithmic_bytes_per_launch": ab["index"],
-            "traffic": measured_traffic(ab["index"]),
+            "traffic": measured_traffic() if cfg.name == "layer_128k" else None,
         },
     }
     if not args.no_cpu_baseline:

@@ -19,6 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmsa.so")
+DRIVER_SRC = os.path.join(PKG, "driver", "msa_counters.cpp")
+DRIVER = os.path.join(PKG, "driver", "msa_counters")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -53,8 +55,13 @@ def build(verbose: bool = False, extra_flags=()) -> str:
     tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, LIB)
+    # the counter driver: a torch-free process for rocprofv3 --pmc runs
+    tmp = DRIVER + ".tmp"
+    _run([HIPCC, *FLAGS, *extra_flags, DRIVER_SRC, "-o", tmp, "-L", PKG, "-lmsa",
+          "-Wl,-rpath,$ORIGIN/.."])
+    os.replace(tmp, DRIVER)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", DRIVER)
     return LIB
 
 

@@ -238,10 +238,10 @@ def _fill(out: torch.Tensor, gen) -> None:
         flat[s:e] = gen(s, e - s).to(flat.dtype)
 
 
-def make_workload(cfg: MSAConfig, device="cpu") -> Workload:
-    device = torch.device(device)
+def layout(cfg: MSAConfig):
+    """(context lengths, blocks per request, block table [B, MAXB]) of a
+    workload, without generating its tensors."""
     T, B = cfg.query_len, cfg.batch
-    R = B * T
     ctx = _ctx_lens(cfg)
     if min(ctx) < T:
         raise ValueError("every context must hold at least decode_query_len tokens")
@@ -255,6 +255,29 @@ def make_workload(cfg: MSAConfig, device="cpu") -> Workload:
     for b in range(B):
         bt[b, :nblk[b]] = phys[off:off + nblk[b]]
         off += nblk[b]
+    return ctx, nblk, bt
+
+
+def write_spec(cfg: MSAConfig, path: str) -> None:
+    """Text description of a workload's shapes, contexts and block table for
+    the counter driver: one header line, B context lengths, B*MAXB table
+    entries."""
+    ctx, nblk, bt = layout(cfg)
+    with open(path, "w") as f:
+        f.write(f"{cfg.batch} {cfg.query_len} {cfg.num_q_heads} {cfg.num_kv_heads} "
+                f"{cfg.num_idx_heads} {cfg.max_blocks} {sum(nblk)} {cfg.kv_dtype} "
+                f"{cfg.idx_dtype} {cfg.topk}\n")
+        f.write(" ".join(str(x) for x in ctx) + "\n")
+        f.write(" ".join(str(int(x)) for x in bt.reshape(-1)) + "\n")
+
+
+def make_workload(cfg: MSAConfig, device="cpu") -> Workload:
+    device = torch.device(device)
+    T, B = cfg.query_len, cfg.batch
+    R = B * T
+    ctx, nblk, bt = layout(cfg)
+    NB = int(sum(nblk))
+    MAXB = cfg.max_blocks
 
     seed = cfg.seed
     t = {}
