@@ -9,9 +9,10 @@
 //   msa_counters decode <spec> <launches>   msa_decode x launches
 //   msa_counters copy   <MiB>  <launches>   16-byte copy kernel x launches
 //
-// Pool contents are constants (traffic does not depend on values): index
-// keys and queries 1.0, K / V 1.0 (bf16), codes and scales giving 1.0 for
-// fp8 and 4-bit KV.
+// Index keys and queries hold hashed small integers in [-8, 8] (so the
+// selections differ from row to row, as with real data); K / V pool contents
+// are constants (1.0 in every format): the bytes a kernel moves do not
+// depend on them.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -46,6 +47,28 @@ __global__ void fill_u16(uint16_t* p, size_t n, uint16_t v) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (size_t)gridDim.x * blockDim.x)
     p[i] = v;
+}
+
+// Integers in [-8, 8] from a 32-bit hash of the element index, stored as
+// bf16 (BYTES == 2) or e4m3 codes (BYTES == 1); both are exact.
+__device__ uint32_t hash32(uint32_t x) {
+  x ^= x >> 16; x *= 0x7feb352dU; x ^= x >> 15; x *= 0x846ca68bU; x ^= x >> 16;
+  return x;
+}
+__constant__ uint8_t kE4m3Int[17] = {0xD0, 0xCE, 0xCC, 0xCA, 0xC8, 0xC4, 0xC0, 0xB8, 0x00,
+                                     0x38, 0x40, 0x44, 0x48, 0x4A, 0x4C, 0x4E, 0x50};
+template <int BYTES>
+__global__ void fill_small_ints(void* p, size_t n, uint32_t salt) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const int v = (int)(hash32((uint32_t)i ^ salt) % 17u) - 8;
+    if (BYTES == 2) {
+      const float f = (float)v;
+      ((uint16_t*)p)[i] = (uint16_t)(__float_as_uint(f) >> 16);
+    } else {
+      ((uint8_t*)p)[i] = kE4m3Int[v + 8];
+    }
+  }
 }
 
 __global__ void fill_f32(float* p, size_t n, float v) {
@@ -125,15 +148,14 @@ int main(int argc, char** argv) {
   t.ctx_lens = d_ctx;
   t.block_table = d_bt;
   uint16_t* iq = (uint16_t*)dalloc(R * Hidx * 64 * 2);
-  hipLaunchKernelGGL(fill_u16, dim3(256), dim3(256), 0, 0, iq, R * Hidx * 64, (uint16_t)0x3F80);
+  hipLaunchKernelGGL(fill_small_ints<2>, dim3(256), dim3(256), 0, 0, iq, R * Hidx * 64, 17u);
   t.idx_q = iq;
-  const size_t ik_bytes = (size_t)NB * Hidx * 128 * 64 * ie;
-  void* ik = dalloc(ik_bytes);
+  const size_t ik_elems = (size_t)NB * Hidx * 128 * 64;
+  void* ik = dalloc(ik_elems * ie);
   if (ie == 2)
-    hipLaunchKernelGGL(fill_u16, dim3(4096), dim3(256), 0, 0, (uint16_t*)ik, ik_bytes / 2,
-                       (uint16_t)0x3F80);
+    hipLaunchKernelGGL(fill_small_ints<2>, dim3(4096), dim3(256), 0, 0, ik, ik_elems, 91u);
   else
-    CHECK(hipMemset(ik, 0x38, ik_bytes));  // e4m3 1.0
+    hipLaunchKernelGGL(fill_small_ints<1>, dim3(4096), dim3(256), 0, 0, ik, ik_elems, 91u);
   t.idx_k_pool = ik;
   float* scores = (float*)dalloc(R * MAXB * 4);
 
