@@ -10,19 +10,24 @@
 // of the KV allocation, never a copy.
 //
 // Design (gfx950):
-//  * A workgroup of 4, 8 or 16 waves owns one (row, KV head, split).  Each
-//    wave walks chunks of 32 keys (two 16-token pages) of the row's page
-//    table; when a workgroup holds the whole row it writes the output itself.
+//  * A workgroup of 4 or 8 waves owns one (row, KV head, split).  Each wave
+//    walks chunks of 32 keys (two 16-token pages) of the row's blocks; when
+//    a workgroup holds the whole row it writes the output itself.  Draft
+//    rows of one request run on one XCD, so blocks they share are read from
+//    HBM once and from L2 after.
 //  * QK^T on MFMA v_mfma_f32_16x16x32_bf16 with keys as the M dimension and
-//    the GQA group's query heads (up to 16) as N: S^T = K Q^T.  K rows go
-//    straight from HBM into the A operand (each lane 64 contiguous bytes of
+//    the query heads of the KV head as N (one tile of 16): S^T = K Q^T; keys
+//    past the row's position are masked.  K rows go straight from HBM into
+//    the A operand (each lane 64 contiguous bytes of
 //    one key row); the result leaves every lane with 4 keys of one head, so
 //    the softmax statistics of a head never cross lane groups but four.
 //  * P V on the same MFMA as O^T = V^T P^T.  P^T is exactly the S^T
 //    accumulator layout (no shuffle); V^T needs a transpose, so the V pages
-//    are staged through LDS (row stride 264 B keeps the four lane groups on
-//    disjoint banks) and read back column-wise.  P is split into bf16 hi + lo
-//    halves (two MFMAs) so the weights keep ~16 bits.
+//    are staged through LDS and read back column-wise (16-byte slots of a
+//    row are XOR-swizzled so the four lane groups of a read hit disjoint
+//    banks).  bf16 V goes from HBM to LDS with direct global-to-LDS loads
+//    and occupies no registers.  P is split into bf16 hi + lo halves (two
+//    MFMAs) so the weights keep ~16 bits.
 //  * fp8 K/V: e4m3 -> bf16 is exact; the per-token K scale multiplies the
 //    logit, the V scale multiplies P.  4-bit K/V: e2m1 x e4m3 -> bf16 is
 //    exact (at most 6 significant bits) and happens in registers.
@@ -40,10 +45,20 @@ namespace msa {
 namespace {
 
 constexpr int kD = 128;          // head dim
-constexpr int kVRow = 264;       // LDS bytes per staged V row (256 + 8 pad)
+constexpr int kVRow = 256;       // LDS bytes per staged V row (bf16)
 constexpr int kChunk = 32;       // keys per chunk (two pages)
-constexpr int kStage = kChunk * kVRow;  // LDS bytes per wave
+constexpr int kStage = kChunk * kVRow;  // LDS bytes of one wave's staged V
+// LDS bytes per wave: the V stage, reused after the chunk loop as the merge
+// area (m and l of 16 columns, 16 output rows of kORow floats).
 constexpr int kORow = 129;       // floats per head row in the merge area
+constexpr int kWaveLds = 8448;
+static_assert(kWaveLds >= kStage && kWaveLds >= 4 * (32 + 16 * kORow), "LDS per wave");
+// s_waitcnt operand (gfx9 encoding) that waits for vmcnt == 0 only.
+constexpr int kWaitVmem = 0x0F70;
+// Cache-policy operand of a direct-to-LDS load: non-temporal.
+constexpr int kNonTemporal = 2;
+
+typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ float neg_inf() { return -INFINITY; }
 
@@ -53,11 +68,17 @@ __device__ __forceinline__ int kappa(int g4, int jj) {
   return jj < 4 ? 4 * g4 + jj : 16 + 4 * g4 + (jj - 4);
 }
 
+// Staged V rows are 256 bytes of 16 slots of 8 dims.  Slot s of row k sits
+// at physical slot s ^ vswz(k), so that the 4 row groups one V^T read
+// touches (rows 4 g4 + c, see kappa) land on distinct banks.
+__device__ __forceinline__ int vswz(int k) { return 2 * ((k >> 2) & 3); }
+__device__ __forceinline__ int voff(int k, int slot) { return k * kVRow + 16 * (slot ^ vswz(k)); }
+
 template <int KV>
 struct Chunk {
   // raw loads of one page: K part for this lane's key row / V part
   u32x4 k[KV == 0 ? 4 : (KV == 1 ? 2 : 1)];
-  u32x4 v[KV == 0 ? 4 : (KV == 1 ? 2 : 1)];
+  u32x4 v[KV == 1 ? 2 : 1];  // bf16 V goes straight to LDS
   uint32_t ks, vs;  // nvfp4: the two e4m3 scale codes of this lane's 32 dims
   f32x4 kscale, vscale;  // fp8: per-token scales of this lane's 4 S^T rows
 };
@@ -73,10 +94,20 @@ __device__ __forceinline__ int kdim(int g, int kk) {
   else return 32 * g + 8 * kk;                                            // whole 64 B row
 }
 
-// Loads of one 16-token page.  K: lane (key m = lane % 16, group g) holds the
-// slices kdim(g, .) of key m.  V: each load instruction covers a contiguous
-// 1 KB run of the page (bf16, fp8) or the whole page (4-bit).
-template <int KV>
+// KV pages of one call are read once when every workgroup owns distinct
+// pages (non-temporal hint), and kept cacheable when row groups of a
+// request share them.
+template <bool STREAM>
+__device__ __forceinline__ u32x4 ld16(const uint8_t* p) {
+  if constexpr (STREAM) return ldg128_stream(p);
+  else return ldg128(p);
+}
+
+// Register loads of one 16-token page.  K: lane (key m = lane % 16, group
+// g) holds the slices kdim(g, .) of key m.  fp8 / 4-bit V: each load
+// instruction covers a contiguous run (1 KB for fp8, the whole page for
+// 4-bit), widened to bf16 by stage_v.  bf16 V takes load_v_lds instead.
+template <int KV, bool STREAM>
 __device__ __forceinline__ void load_page(Chunk<KV>& c, const uint8_t* __restrict__ k_pool,
                                           const uint8_t* __restrict__ v_pool,
                                           const void* __restrict__ k_scale,
@@ -85,28 +116,41 @@ __device__ __forceinline__ void load_page(Chunk<KV>& c, const uint8_t* __restric
   const int m = lane & 15, g = lane >> 4;
   if constexpr (KV == 0) {
     const uint8_t* kp = k_pool + (row0 + m) * 256 + 16 * g;
-    const uint8_t* vp = v_pool + row0 * 256 + 16 * lane;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) c.k[i] = ldg128_stream(kp + 64 * i);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) c.v[i] = ldg128_stream(vp + 1024 * i);
+    for (int i = 0; i < 4; ++i) c.k[i] = ld16<STREAM>(kp + 64 * i);
   } else if constexpr (KV == 1) {
     const uint8_t* kp = k_pool + (row0 + m) * 128 + 16 * g;
     const uint8_t* vp = v_pool + row0 * 128 + 16 * lane;
-    c.k[0] = ldg128_stream(kp);
-    c.k[1] = ldg128_stream(kp + 64);
-    c.v[0] = ldg128_stream(vp);
-    c.v[1] = ldg128_stream(vp + 1024);
+    c.k[0] = ld16<STREAM>(kp);
+    c.k[1] = ld16<STREAM>(kp + 64);
+    c.v[0] = ld16<STREAM>(vp);
+    c.v[1] = ld16<STREAM>(vp + 1024);
     c.kscale = *reinterpret_cast<const f32x4*>(static_cast<const float*>(k_scale) + row0 + 4 * g);
     c.vscale = *reinterpret_cast<const f32x4*>(static_cast<const float*>(v_scale) + row0 + 4 * g);
   } else {
-    c.k[0] = ldg128_stream(k_pool + (row0 + m) * 64 + 16 * g);
-    c.v[0] = ldg128_stream(v_pool + row0 * 64 + 16 * lane);
+    c.k[0] = ld16<STREAM>(k_pool + (row0 + m) * 64 + 16 * g);
+    c.v[0] = ld16<STREAM>(v_pool + row0 * 64 + 16 * lane);
     c.ks = *reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(k_scale) +
                                               (row0 + m) * 8 + 2 * g);
     c.vs = *reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(v_scale) +
                                               (row0 + (lane >> 2)) * 8 + 2 * (lane & 3));
   }
+}
+
+// bf16 V of one page straight from HBM into its LDS rows, no registers
+// involved.  Load i fills rows 4i..4i+3 (1 KB, 16 bytes per lane at LDS
+// offset 16 lane); a lane fetches the global slot that the swizzle puts
+// there (vswz of those rows is 2i).  Issued after the K loads so that
+// waiting for K does not wait for V.
+template <bool STREAM>
+__device__ __forceinline__ void load_v_lds(const uint8_t* __restrict__ v_pool, size_t row0,
+                                           int lane, uint8_t* page_rows) {
+  const uint8_t* vp = v_pool + (row0 + (lane >> 4)) * 256;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    __builtin_amdgcn_global_load_lds(vp + 1024 * i + 16 * ((lane & 15) ^ (2 * i)),
+                                     (lds_void*)(page_rows + 1024 * i), 16, 0,
+                                     STREAM ? kNonTemporal : 0);
 }
 
 // Four packed bf16 pairs from 8 e2m1 codes (one dword) with scale `s`.
@@ -154,13 +198,7 @@ __device__ __forceinline__ void lds_write16(uint8_t* dst, uint32_t a, uint32_t b
 // kVRow bytes apart), converting fp8 / e2m1 to bf16 on the way.
 template <int KV>
 __device__ __forceinline__ void stage_v(const Chunk<KV>& c, uint8_t* page_rows, int lane) {
-  if constexpr (KV == 0) {
-    // load i: key 4i + lane/16, dims 8*(lane%16)..+8
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      lds_write16(page_rows + (4 * i + (lane >> 4)) * kVRow + 16 * (lane & 15), c.v[i].x,
-                  c.v[i].y, c.v[i].z, c.v[i].w);
-  } else if constexpr (KV == 1) {
+  if constexpr (KV == 1) {
     // load i: key 8i + lane/8, dims 16*(lane%8)..+16
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -171,92 +209,117 @@ __device__ __forceinline__ void stage_v(const Chunk<KV>& c, uint8_t* page_rows, 
         o[2 * w] = e4m3x2_to_bf16x2<false>(src[w]);
         o[2 * w + 1] = e4m3x2_to_bf16x2<true>(src[w]);
       }
-      uint8_t* dst = page_rows + (8 * i + (lane >> 3)) * kVRow + 32 * (lane & 7);
+      // slots 2 (lane % 8) and the next stay adjacent under the swizzle
+      const int k = 8 * i + (lane >> 3);
+      uint8_t* dst = page_rows + voff(k, 2 * (lane & 7));
       lds_write16(dst, o[0], o[1], o[2], o[3]);
       lds_write16(dst + 16, o[4], o[5], o[6], o[7]);
     }
-  } else {
+  } else if constexpr (KV == 2) {
     // key lane/4, dims 32*(lane%4)..+32
     const uint32_t src[4] = {c.v[0].x, c.v[0].y, c.v[0].z, c.v[0].w};
     const float s0 = e4m3_to_f32(c.vs & 0xFFu);
     const float s1 = e4m3_to_f32((c.vs >> 8) & 0xFFu);
-    uint8_t* dst = page_rows + (lane >> 2) * kVRow + 64 * (lane & 3);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       uint32_t o[4];
       e2m1x8_to_bf16(src[w], w < 2 ? s0 : s1, o);
-      lds_write16(dst + 16 * w, o[0], o[1], o[2], o[3]);
+      lds_write16(page_rows + voff(lane >> 2, 4 * (lane & 3) + w), o[0], o[1], o[2], o[3]);
     }
   }
 }
 
-template <int KV, int W>
+// One workgroup owns (row r = b T + t, KV head g, split): the G query heads
+// of KV head g are the MFMA columns (zero past G), the row's page table
+// lists its blocks, local block last.  Every wave walks chunks of 32 keys
+// (two 16-token pages) of the row's blocks, S apart between the splits and
+// S W apart between the waves of a split.
+template <int KV, int W, bool STREAM>
 __global__ __launch_bounds__(64 * W, 4) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ k_pool,
     const uint8_t* __restrict__ v_pool, const void* __restrict__ k_scale,
     const void* __restrict__ v_scale, const int32_t* __restrict__ page_table,
     const int32_t* __restrict__ ctx_lens, float* __restrict__ part_o,
-    float* __restrict__ part_ml, float* __restrict__ out, int T, int Hq, int Hkv, int PT, int S,
-    int cpw, int max_page, float scale_log2) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[W * kStage];
+    float* __restrict__ part_ml, float* __restrict__ out, int B, int T, int Hq, int Hkv, int PT,
+    int S, int max_block, float scale_log2) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[W * kWaveLds];
 
   const int lane = lane_id();
   const int wave = wave_id();
-  const int wid = blockIdx.x;
-  const int split = wid % S;
-  const int rg = wid / S;
-  const int g = rg % Hkv;
-  const int r = rg / Hkv;
-  const int b = r / T;
-  const int t = r - b * T;
+  // Workgroup ids go round-robin over the 8 XCDs.  With several draft rows
+  // per request (T > 1), which select mostly the same blocks, ids are
+  // permuted so that all of request b's workgroups run on XCD b % 8 and
+  // meet in its L2; otherwise ids are request-major.
+  const int per = T * Hkv * S;
+  int b, x;
+  if (T > 1) {
+    b = (blockIdx.x / (8 * per)) * 8 + (blockIdx.x & 7);
+    x = (blockIdx.x >> 3) % per;
+  } else {
+    b = blockIdx.x / per;
+    x = blockIdx.x % per;
+  }
+  if (b >= B) return;
+  const int split = x % S;
+  x /= S;
+  const int g = x % Hkv;
+  const int t = x / Hkv;
+  const int r = b * T + t;
   const int G = Hq / Hkv;
-  const int pos = ctx_lens[b] - T + t;
 
-  // valid pages of the row (the table is -1 padded at the end)
-  const int32_t* prow = page_table + (size_t)r * PT;
-  const int pt_lo = lane < PT ? prow[lane] : -1;
-  const int pt_hi = lane + kWave < PT ? prow[lane + kWave] : -1;
-  const int nvp = __popcll(__ballot(pt_lo >= 0)) + __popcll(__ballot(pt_hi >= 0));
-  const int nblk = nvp >> 3;
-  const int kv_len = nblk > 0 ? 128 * (nblk - 1) + (pos & 127) + 1 : 0;
-
-  // Q^T operand: lane holds head (lane & 15) of the group, dims 32*(lane>>4)..+32
+  // Q^T operand: column hl is query head g G + hl of row r (zero past G);
+  // lane group g4 holds the dims kdim(g4, kk) of K-step kk
   const int hl = lane & 15;
   const int g4 = lane >> 4;
   bf16x8 qop[4];
   {
-    u32x4 z = {0u, 0u, 0u, 0u};
+    const u32x4 z = {0u, 0u, 0u, 0u};
     const uint16_t* qp = q + ((size_t)r * Hq + g * G + min(hl, G - 1)) * kD;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      u32x4 v = ldg128(qp + kdim<KV>(g4, kk));
+      const u32x4 v = ldg128(qp + kdim<KV>(g4, kk));
       qop[kk] = __builtin_bit_cast(bf16x8, hl < G ? v : z);
     }
   }
+
+  // the row's page table stays in registers: slot k's first page in lane 8k
+  const int32_t* prow = page_table + (size_t)r * PT;
+  const int pt_lo = lane < PT ? prow[lane] : -1;
+  const int pt_hi = lane + kWave < PT ? prow[lane + kWave] : -1;
+  const int nblk = (__popcll(__ballot(pt_lo >= 0)) + __popcll(__ballot(pt_hi >= 0))) >> 3;
+  // keys of the local block that are causal to the row (position L - T + t)
+  const int vloc = ((ctx_lens[b] - T + t) & 127) + 1;
 
   float m = neg_inf(), lsum = 0.f;
   f32x4 oacc[8];
 #pragma unroll
   for (int s = 0; s < 8; ++s) oacc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  uint8_t* stage = smem + wave * kStage;
-  const size_t kv_head_rows = 128;
-  for (int k = 0; k < cpw; ++k) {
-    const int ci = split * W * cpw + wave + W * k;
-    if (ci * kChunk >= kv_len) break;
+  uint8_t* stage = smem + wave * kWaveLds;
+  const int nchunks = 4 * nblk;  // 4 chunks of 32 keys per block
+  for (int ci = split + S * wave; ci < nchunks; ci += S * W) {
+    const int u = ci >> 2;         // block slot in the row's table
+    const int pg0 = (ci & 3) * 2;  // first page of the chunk inside the block
+    const bool local = u == nblk - 1;
+    if (local && 32 * (ci & 3) >= vloc) continue;  // past the row's position
+    const int idx = 8 * u;                         // wave-uniform
+    const int P = idx < kWave ? __builtin_amdgcn_readlane(pt_lo, idx)
+                              : __builtin_amdgcn_readlane(pt_hi, idx - kWave);
+    const int phys = min(max(P >> 3, 0), max_block);  // a bad table cannot leave the pools
+    const size_t row0 = ((size_t)phys * Hkv + g) * 128 + (size_t)pg0 * 16;
     Chunk<KV> ch[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int idx = 2 * ci + j;  // wave-uniform
-      int P = idx < kWave ? __builtin_amdgcn_readlane(pt_lo, idx)
-                          : __builtin_amdgcn_readlane(pt_hi, idx - kWave);
-      P = min(max(P, 0), max_page);  // a malformed table cannot reach outside the pools
-      const size_t row0 = ((size_t)(P >> 3) * Hkv + g) * kv_head_rows + (size_t)(P & 7) * 16;
-      load_page<KV>(ch[j], k_pool, v_pool, k_scale, v_scale, row0, lane);
-    }
-    // stage the two V pages into LDS rows 0..15 and 16..31
+    for (int j = 0; j < 2; ++j)
+      load_page<KV, STREAM>(ch[j], k_pool, v_pool, k_scale, v_scale, row0 + 16 * j, lane);
+    if constexpr (KV == 0) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) stage_v<KV>(ch[j], stage + 16 * j * kVRow, lane);
+      for (int j = 0; j < 2; ++j)
+        load_v_lds<STREAM>(v_pool, row0 + 16 * j, lane, stage + 16 * j * kVRow);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) stage_v<KV>(ch[j], stage + 16 * j * kVRow, lane);
+    }
+
     // S^T = K Q^T for the two pages
     f32x4 sacc[2];
 #pragma unroll
@@ -267,7 +330,9 @@ __global__ __launch_bounds__(64 * W, 4) void sparse_attn_kernel(
         sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<KV>(ch[j], kk), qop[kk],
                                                           sacc[j], 0, 0, 0);
     }
-    // online softmax over this chunk (log2 domain)
+    // online softmax over the chunk (log2 domain); keys past the row's
+    // position in its local block, and columns past G, are masked
+    const int lim = hl < G ? (local ? vloc : 128) : 0;
     float z[8];
     float mc = neg_inf();
 #pragma unroll
@@ -276,8 +341,8 @@ __global__ __launch_bounds__(64 * W, 4) void sparse_attn_kernel(
       for (int i = 0; i < 4; ++i) {
         float v = sacc[j][i] * scale_log2;
         if constexpr (KV == 1) v *= ch[j].kscale[i];
-        const int n = ci * kChunk + 16 * j + 4 * g4 + i;
-        v = n < kv_len ? v : neg_inf();
+        const int tok = 16 * (pg0 + j) + 4 * g4 + i;
+        v = tok < lim ? v : neg_inf();
         z[4 * j + i] = v;
         mc = fmaxf(mc, v);
       }
@@ -308,13 +373,15 @@ __global__ __launch_bounds__(64 * W, 4) void sparse_attn_kernel(
 #pragma unroll
     for (int s = 0; s < 8; ++s) oacc[s] *= alpha;
 
+    if constexpr (KV == 0) __builtin_amdgcn_s_waitcnt(kWaitVmem);  // V rows landed in LDS
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     // O^T += V^T P^T, dims in blocks of 16
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const uint8_t* col = stage + (16 * s + hl) * 2;
+      // dim 16 s + hl of rows kappa(g4, .), all with vswz = 2 g4
+      const uint8_t* col = stage + 32 * (s ^ g4) + 2 * hl;
       uint32_t a[4];
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
@@ -334,7 +401,7 @@ __global__ __launch_bounds__(64 * W, 4) void sparse_attn_kernel(
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
 
-  // combine the W waves in LDS
+  // ---- combine the W waves in LDS (the stage areas are free now)
   __syncthreads();
   float* m_w = reinterpret_cast<float*>(smem);  // [W][16]
   float* l_w = m_w + 16 * W;                    // [W][16]
@@ -408,17 +475,24 @@ __global__ void selftest_kernel(float* out) {
   }
 }
 
-template <int KV, int W>
+// Workgroups of one launch; with T > 1 the request count is padded to a
+// multiple of 8 for the XCD-aware id mapping.
+long attention_workgroups(const Dims& d, const SplitPlan& sp) {
+  const long reqs = d.T > 1 ? (d.B + 7) / 8 * 8 : d.B;
+  return reqs * d.T * d.Hkv * sp.splits;
+}
+
+template <int KV, int W, bool STREAM>
 hipError_t launch_kvw(const Dims& d, const SplitPlan& sp, const void* q, const void* k_pool,
                       const void* v_pool, const void* k_scale, const void* v_scale,
                       const int32_t* page_table, const int32_t* ctx_lens, float* part_o,
                       float* part_ml, float* out, hipStream_t s) {
-  const long wgs = (long)d.R() * d.Hkv * sp.splits;
-  hipLaunchKernelGGL((sparse_attn_kernel<KV, W>), dim3((unsigned)wgs), dim3(64 * W), 0, s,
+  hipLaunchKernelGGL((sparse_attn_kernel<KV, W, STREAM>),
+                     dim3((unsigned)attention_workgroups(d, sp)), dim3(64 * W), 0, s,
                      static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(k_pool),
                      static_cast<const uint8_t*>(v_pool), k_scale, v_scale, page_table,
-                     ctx_lens, part_o, part_ml, out, d.T, d.Hq, d.Hkv, d.PT(), sp.splits,
-                     sp.cpw, d.NB * 8 - 1, d.scale_log2);
+                     ctx_lens, part_o, part_ml, out, d.B, d.T, d.Hq, d.Hkv, d.PT(), sp.splits,
+                     d.NB - 1, d.scale_log2);
   return hipGetLastError();
 }
 
@@ -427,32 +501,35 @@ hipError_t launch_kv(const Dims& d, const SplitPlan& sp, const void* q, const vo
                      const void* v_pool, const void* k_scale, const void* v_scale,
                      const int32_t* page_table, const int32_t* ctx_lens, float* part_o,
                      float* part_ml, float* out, hipStream_t s) {
-  if (sp.waves == 16)
-    return launch_kvw<KV, 16>(d, sp, q, k_pool, v_pool, k_scale, v_scale, page_table, ctx_lens,
-                              part_o, part_ml, out, s);
-  if (sp.waves == 8)
-    return launch_kvw<KV, 8>(d, sp, q, k_pool, v_pool, k_scale, v_scale, page_table, ctx_lens,
-                             part_o, part_ml, out, s);
-  return launch_kvw<KV, 4>(d, sp, q, k_pool, v_pool, k_scale, v_scale, page_table, ctx_lens,
-                           part_o, part_ml, out, s);
+#define MSA_ATTN(WV, ST)                                                                  \
+  return launch_kvw<KV, WV, ST>(d, sp, q, k_pool, v_pool, k_scale, v_scale, page_table, \
+                                ctx_lens, part_o, part_ml, out, s)
+  // One row per request: every page is read once, with the non-temporal
+  // hint.  Several draft rows: cached loads, so that rows sharing a block
+  // meet in L2.
+  if (d.T == 1) {
+    if (sp.waves == 8) MSA_ATTN(8, true);
+    MSA_ATTN(4, true);
+  }
+  if (sp.waves == 8) MSA_ATTN(8, false);
+  MSA_ATTN(4, false);
+#undef MSA_ATTN
 }
 
 }  // namespace
 
 SplitPlan plan_splits(const Dims& d) {
-  // At least one workgroup per CU (256), split a row's chunks only as far as
-  // needed, and keep >= 4 chunks per split; waves per workgroup follow the
-  // chunks a split holds.  The 128K layer (256 row x KV-head pairs) gets one
-  // 16-wave workgroup per pair and no merge pass.
-  const int chunks = d.PT() / 2;
+  // One workgroup per (row, KV head, split).  Rows are split only until
+  // there is one workgroup per CU (256), keeping at least one chunk of 32
+  // keys per wave of 8.  On MI355X 8 waves per workgroup measured faster
+  // than 4 or 16, and fewer splits faster than more (less merging).
+  SplitPlan p;
+  const int chunks = 4 * d.topk;  // at most 4 chunks per selected block
   const long pairs = (long)d.R() * d.Hkv;
   int S = 1;
-  while (S * 2 <= chunks / 4 && pairs * S < 256) S *= 2;
-  const int per_split = (chunks + S - 1) / S;
-  SplitPlan p;
+  while (S * 2 <= chunks / 8 && pairs * S < 256) S *= 2;
   p.splits = S;
-  p.waves = per_split >= 16 ? 16 : (per_split >= 8 ? 8 : 4);
-  p.cpw = (per_split + p.waves - 1) / p.waves;
+  p.waves = (chunks + S - 1) / S >= 8 ? 8 : 4;
   return p;
 }
 
@@ -476,9 +553,8 @@ hipError_t launch_sparse_attention(const Dims& d, const void* q, const void* k_p
   static const char* names[3] = {"bf16", "fp8", "nvfp4"};
   if (note)
     *note += std::string("sparse_attn<") + names[d.kv_dtype] + ">[grid=" +
-             std::to_string((long)d.R() * d.Hkv * sp.splits) + "x" + std::to_string(64 * sp.waves) +
-             ",splits=" + std::to_string(sp.splits) + ",chunks_per_wave=" +
-             std::to_string(sp.cpw) + "]";
+             std::to_string(attention_workgroups(d, sp)) + "x" + std::to_string(64 * sp.waves) +
+             ",splits=" + std::to_string(sp.splits) + "]";
   if (sp.splits > 1) {
     const unsigned rows = (unsigned)((long)d.R() * d.Hq);
     hipLaunchKernelGGL(lse_merge_kernel, dim3(rows), dim3(kD), 0, s, part_o, part_ml, out,

@@ -21,12 +21,10 @@ struct Dims {
   int PT() const { return topk * 8; }  // page-table row length
 };
 
-// Attention split plan: a workgroup of `waves` waves covers waves * cpw
-// chunks of 32 keys (two 16-token pages) of one (row, KV head); `splits`
-// workgroups per (row, KV head) together cover the row's page table.
+// Attention plan: one workgroup of `waves` waves per (row, KV head, split);
+// the `splits` workgroups of a (row, KV head) share its chunks of 32 keys.
 struct SplitPlan {
-  int waves;   // waves per workgroup: 4, 8 or 16
-  int cpw;     // chunks per wave
+  int waves;   // waves per workgroup: 4 or 8
   int splits;  // workgroups per (row, KV head)
 };
 SplitPlan plan_splits(const Dims& d);
