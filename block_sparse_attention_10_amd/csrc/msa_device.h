@@ -89,34 +89,4 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// One DPP step of a wave reduction: max with the lane the pattern names
-// (lanes outside `row_mask` keep their value).
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ uint32_t dpp_max_u32(uint32_t v) {
-  const uint32_t o =
-      (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROW_MASK, 0xF, false);
-  return o > v ? o : v;
-}
-
-// Wave-wide unsigned max, returned to every lane: DPP within rows of 16
-// (quad swaps, half-row and row mirrors), row broadcasts across rows, then
-// lane 63 holds the result.
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  v = dpp_max_u32<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
-  v = dpp_max_u32<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
-  v = dpp_max_u32<0x141, 0xF>(v);  // row_half_mirror
-  v = dpp_max_u32<0x140, 0xF>(v);  // row_mirror
-  v = dpp_max_u32<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
-  v = dpp_max_u32<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
-  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
-}
-
-// Wave-wide max of 64-bit keys via two 32-bit passes (high word, then the
-// low word among the lanes holding the high maximum).
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  const uint32_t hi = wave_max_u32((uint32_t)(v >> 32));
-  const uint32_t lo = wave_max_u32((uint32_t)(v >> 32) == hi ? (uint32_t)v : 0u);
-  return ((uint64_t)hi << 32) | lo;
-}
-
 }  // namespace msa
