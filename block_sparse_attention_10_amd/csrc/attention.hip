@@ -209,22 +209,38 @@ __device__ __forceinline__ void stage_v(const Chunk<KV>& c, uint8_t* page_rows, 
         o[2 * w] = e4m3x2_to_bf16x2<false>(src[w]);
         o[2 * w + 1] = e4m3x2_to_bf16x2<true>(src[w]);
       }
-      // slots 2 (lane % 8) and the next stay adjacent under the swizzle
+      // Slots 2 (lane % 8) and the next stay adjacent under the swizzle.
+      // Which of the two a lane writes first alternates with bit 2 of the
+      // lane and with the row, so that any 8 consecutive lanes write 8
+      // distinct 16-byte slots modulo 128 bytes and any 16 lanes (two
+      // rows) 16 distinct slots modulo 256 bytes: no bank conflicts on the
+      // 128-bit LDS writes whichever lane grouping serves them.
       const int k = 8 * i + (lane >> 3);
+      const bool odd = ((lane >> 2) ^ k) & 1;
       uint8_t* dst = page_rows + voff(k, 2 * (lane & 7));
-      lds_write16(dst, o[0], o[1], o[2], o[3]);
-      lds_write16(dst + 16, o[4], o[5], o[6], o[7]);
+      lds_write16(dst + (odd ? 16 : 0), odd ? o[4] : o[0], odd ? o[5] : o[1],
+                  odd ? o[6] : o[2], odd ? o[7] : o[3]);
+      lds_write16(dst + (odd ? 0 : 16), odd ? o[0] : o[4], odd ? o[1] : o[5],
+                  odd ? o[2] : o[6], odd ? o[3] : o[7]);
     }
   } else if constexpr (KV == 2) {
     // key lane/4, dims 32*(lane%4)..+32
     const uint32_t src[4] = {c.v[0].x, c.v[0].y, c.v[0].z, c.v[0].w};
     const float s0 = e4m3_to_f32(c.vs & 0xFFu);
     const float s1 = e4m3_to_f32((c.vs >> 8) & 0xFFu);
+    // Write w of a lane stores a rotated piece pc, so that any 8
+    // consecutive lanes (two rows) write 8 distinct 16-byte slots modulo
+    // 128 bytes and any 16 lanes (four rows) 16 distinct slots modulo 256
+    // bytes: no bank conflicts on the 128-bit LDS writes.
+    const int k = lane >> 2;
+    const int rot = ((lane & 3) >> 1) + 2 * (k & 1) + ((k >> 1) & 1);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
+      const int pc = (w + rot) & 3;
+      const uint32_t word = pc == 0 ? src[0] : (pc == 1 ? src[1] : (pc == 2 ? src[2] : src[3]));
       uint32_t o[4];
-      e2m1x8_to_bf16(src[w], w < 2 ? s0 : s1, o);
-      lds_write16(page_rows + voff(lane >> 2, 4 * (lane & 3) + w), o[0], o[1], o[2], o[3]);
+      e2m1x8_to_bf16(word, pc < 2 ? s0 : s1, o);
+      lds_write16(page_rows + voff(k, 4 * (lane & 3) + pc), o[0], o[1], o[2], o[3]);
     }
   }
 }

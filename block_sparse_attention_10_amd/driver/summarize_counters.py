@@ -10,6 +10,9 @@ still describe the code.
 
     python summarize_counters.py --spec S --fetch F.csv --write W.csv \\
         --copy-fetch CF.csv --copy-write CW.csv --copy-mib 1024 --out OUT.json
+
+With --table and a list of counter_collection CSVs it prints instead a
+markdown table of every counter's mean value per launch, per kernel.
 """
 import argparse
 import collections
@@ -18,6 +21,7 @@ import hashlib
 import json
 import os
 import re
+import sys
 
 PKG = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(PKG, "csrc")
@@ -77,7 +81,31 @@ def index_key_bytes(spec):
     return blocks * spec["Hidx"] * 128 * 64 * elem
 
 
+def counter_table(paths):
+    """Markdown table: mean value per launch of every counter in the given
+    counter_collection CSVs, one row per library kernel."""
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    for path in paths:
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                fam = family_of(r["Kernel_Name"])
+                if fam is None:
+                    continue
+                name = re.sub(r"\(.*", "", r["Kernel_Name"].replace("(anonymous namespace)::", ""))
+                vals[name.replace("void ", "")][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    counters = sorted({c for k in vals.values() for c in k})
+    lines = ["| kernel | " + " | ".join(counters) + " |",
+             "|---|" + "---|" * len(counters)]
+    for name, cs in vals.items():
+        cells = [f"{sum(cs[c]) / len(cs[c]):,.0f}" if c in cs else "" for c in counters]
+        lines.append(f"| {name} | " + " | ".join(cells) + " |")
+    return "\n".join(lines)
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--table":
+        print(counter_table(sys.argv[2:]))
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--spec", required=True)
     ap.add_argument("--workload", required=True)
