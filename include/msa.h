@@ -157,7 +157,12 @@ int msa_build_page_table(const msa_problem* p, const int32_t* selected,
  * per query head, computed split-K with fp32 partials in `workspace` and
  * merged by log-sum-exp.  Reads t->q, t->k_pool, t->v_pool, t->k_scale,
  * t->v_scale, t->ctx_lens.  Page ids are clamped to the pools.  One launch,
- * plus a merge launch when a row is split over several workgroups. */
+ * plus a merge launch when a row is split over several workgroups.
+ * Cross-layer reuse (news.ainew.jp article, section 3, on index sharing:
+ * adjacent sparse layers pick nearly the same blocks, so one layer selects
+ * and later layers reuse its top-k): call this with a later layer's q and
+ * pools and the page table an earlier layer's msa_decode exported; layers
+ * share the block table, so the page ids hold in every layer's pool. */
 int msa_sparse_decode(const msa_problem* p, const msa_tensors* t, const int32_t* page_table,
                       float* out, void* workspace, size_t workspace_bytes, void* stream);
 

@@ -271,7 +271,10 @@ def write_spec(cfg: MSAConfig, path: str) -> None:
         f.write(" ".join(str(int(x)) for x in bt.reshape(-1)) + "\n")
 
 
-def make_workload(cfg: MSAConfig, device="cpu") -> Workload:
+def make_workload(cfg: MSAConfig, device="cpu", layer: int = 0) -> Workload:
+    """The workload's tensors.  `layer` > 0 draws another layer of the same
+    model state: same context lengths and block table (the block table is
+    shared by all layers), fresh queries, keys and values."""
     device = torch.device(device)
     T, B = cfg.query_len, cfg.batch
     R = B * T
@@ -279,7 +282,7 @@ def make_workload(cfg: MSAConfig, device="cpu") -> Workload:
     NB = int(sum(nblk))
     MAXB = cfg.max_blocks
 
-    seed = cfg.seed
+    seed = cfg.seed + 100003 * layer
     t = {}
     t["ctx_lens"] = torch.tensor(ctx, dtype=torch.int32, device=device)
     t["block_table"] = torch.from_numpy(bt).to(device)

@@ -128,6 +128,42 @@ def oracle_rows(w: Workload, rows):
     return res
 
 
+def oracle_attention_rows(w: Workload, rows, selection):
+    """Oracle attention output of the given rows of `w` over a given
+    selection (row -> logical block ids, -1 padded), e.g. one another layer
+    made; compact host pools of just those blocks, request by request."""
+    c = w.cfg
+    T = c.query_len
+    t = w.tensors
+    out = {}
+    by_req = {}
+    for r in rows:
+        by_req.setdefault(r // T, []).append(r)
+    for b, rs in by_req.items():
+        nblk = w.nblk[b]
+        bt_row = t["block_table"][b, :nblk].to(torch.int64)
+        local_rows = np.array([r % T for r in rs], dtype=np.int32)
+        sel = np.full((T, c.topk), -1, dtype=np.int32)
+        for r in rs:
+            sel[r % T] = selection[r]
+        mini = problem_of(c)
+        mini.batch = 1
+        mini.max_blocks = nblk
+        used = sorted({int(x) for x in sel.reshape(-1) if x >= 0})
+        remap = np.zeros(nblk, dtype=np.int32)
+        remap[used] = np.arange(len(used), dtype=np.int32)
+        phys = bt_row[torch.tensor(used, dtype=torch.int64, device=bt_row.device)]
+        kv = {name: None if t[name] is None else _host(t[name][phys])
+              for name in ("k_pool", "v_pool", "k_scale", "v_scale")}
+        o = oracle.attention(mini, _host(t["q"][b * T:(b + 1) * T]), kv["k_pool"], kv["v_pool"],
+                             kv["k_scale"], kv["v_scale"], remap[None, :],
+                             np.array([w.ctx_lens[b]], dtype=np.int32), sel[local_rows],
+                             local_rows)
+        for i, r in enumerate(rs):
+            out[r] = o[i]
+    return out
+
+
 def compare_rows(w: Workload, got, rows, ref=None):
     """Bit-exact scores / selection / page table, tolerance on outputs."""
     c = w.cfg

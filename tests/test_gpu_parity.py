@@ -12,8 +12,8 @@ import torch
 import block_sparse_attention_10_amd as msa
 import oracle
 from synth import CONFIG_ORDER, CONFIGS, make_workload, small_config
-from tests.msa_gpu import (TOL, check_invariants, compare_rows, oracle_rows, problem_for,
-                           run_fused, run_stages, tensors_for)
+from tests.msa_gpu import (TOL, check_invariants, compare_rows, oracle_attention_rows,
+                           oracle_rows, problem_for, run_fused, run_stages, tensors_for)
 
 pytestmark = pytest.mark.gpu
 
@@ -139,6 +139,40 @@ def test_workspace_reuse_across_calls_and_entry_points(kw):
         assert torch.equal(out, ref["out"]), f"call {i}"
         if i % 2 == 0:
             assert torch.equal(sel, ref["selected"]) and torch.equal(pt, ref["page_table"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(batch=3, query_len=2, ctx_lo=3000, ctx_hi=20000, num_q_heads=16, num_kv_heads=2,
+         num_idx_heads=2, seed=21),
+    dict(batch=2, query_len=1, ctx_lo=5000, ctx_hi=30000, kv_dtype="fp8", idx_dtype="fp8",
+         seed=22),
+])
+def test_cross_layer_reuse_of_the_selection(kw):
+    """Index sharing across adjacent sparse layers: layer 0 selects, layer 1
+    attends over layer 0's page table through msa_sparse_decode (no scan, no
+    selection of its own).  The block table is shared by the layers."""
+    cfg = small_config(**kw)
+    w0 = make_workload(cfg, DEV)
+    w1 = make_workload(cfg, DEV, layer=1)
+    assert torch.equal(w0.tensors["block_table"], w1.tensors["block_table"])
+    rows = list(range(cfg.rows))
+    ref0 = oracle_rows(w0, rows)
+    a = run_fused(w0)
+    compare_rows(w0, a, rows, ref0)
+    p1 = problem_for(w1)
+    t1 = tensors_for(w1)
+    out1 = torch.empty_like(a["out"])
+    ws = torch.empty((msa.msa_workspace_bytes(p1),), dtype=torch.uint8, device=DEV)
+    msa.msa_sparse_decode(p1, t1, a["page_table"], out1, ws)
+    torch.cuda.synchronize()
+    ref1 = oracle_attention_rows(w1, rows, {r: ref0[r]["selected"] for r in rows})
+    got = out1.cpu().numpy().astype(np.float64)
+    err = max(float(np.max(np.abs(got[r] - ref1[r]))) for r in rows)
+    assert err <= TOL[cfg.kv_dtype], err
+    # reuse is a real change of work: layer 1 would have selected differently
+    own = oracle_rows(w1, rows)
+    assert any(not np.array_equal(own[r]["selected"], ref0[r]["selected"]) for r in rows)
+    _say(f"  reuse max abs err {err:.3g}")
 
 
 def test_workspace_too_small_is_rejected():
