@@ -120,7 +120,7 @@ typedef struct {
   int32_t topk;         /* blocks kept per query row (16)               */
   int32_t max_blocks;   /* block_table row length                       */
   int32_t kv_dtype;     /* ORACLE_BF16 / ORACLE_FP8 / ORACLE_NVFP4      */
-  int32_t idx_dtype;    /* ORACLE_BF16 / ORACLE_FP8                     */
+  int32_t idx_dtype;    /* ORACLE_BF16 / ORACLE_FP8 / ORACLE_NVFP4      */
   double sm_scale;      /* 0 means 1/sqrt(head_dim)                     */
 } oracle_problem;
 
@@ -129,13 +129,24 @@ static int64_t row_position(int32_t ctx_len, int32_t T, int32_t t) {
   return (int64_t)ctx_len - T + t;
 }
 
-/* Index key element (token i of logical block c, index head h, dim d). */
+/* Index key element (token tok of physical block phys, index head h, dim
+ * d): bf16 as is, fp8 e4m3 code as is (no scale), or 4-bit: the E2M1 code
+ * times the E4M3 scale of its group of 16 dims (idx_k_scale), the key
+ * format the pages name next for the index cache (aisoku.org article,
+ * section "何が新しいか": NVFP4 storage). */
 static double idx_key_value(const oracle_problem* p, const void* idx_k_pool,
-                            int64_t phys, int h, int tok, int d) {
-  int64_t off = (((phys * p->num_idx_heads + h) * p->block_size) + tok) * p->idx_dim + d;
+                            const void* idx_k_scale, int64_t phys, int h, int tok, int d) {
+  int64_t row = (phys * p->num_idx_heads + h) * p->block_size + tok;
+  int E = p->idx_dim;
   if (p->idx_dtype == ORACLE_BF16)
-    return msa_oracle_bf16_to_double(((const uint16_t*)idx_k_pool)[off]);
-  return msa_oracle_e4m3_to_double(((const uint8_t*)idx_k_pool)[off]);
+    return msa_oracle_bf16_to_double(((const uint16_t*)idx_k_pool)[row * E + d]);
+  if (p->idx_dtype == ORACLE_FP8)
+    return msa_oracle_e4m3_to_double(((const uint8_t*)idx_k_pool)[row * E + d]);
+  /* 4-bit: byte j of the row holds elements 2j (low nibble), 2j+1 (high). */
+  uint8_t byte = ((const uint8_t*)idx_k_pool)[row * (E / 2) + d / 2];
+  uint8_t nib = (d & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 0xF);
+  uint8_t sc = ((const uint8_t*)idx_k_scale)[row * (E / 16) + d / 16];
+  return msa_oracle_e2m1_to_double(nib) * msa_oracle_e4m3_to_double(sc);
 }
 
 /* One K or V element, dequantised: bf16 as is; fp8 code times the token's
@@ -165,7 +176,8 @@ static double kv_value(const oracle_problem* p, const void* pool, const void* sc
  * block score -inf.  `rows` lists the query rows to compute (NULL = all);
  * scores is [nrows][max_blocks]. */
 int msa_oracle_index_scores(const oracle_problem* p, const uint16_t* idx_q,
-                            const void* idx_k_pool, const int32_t* block_table,
+                            const void* idx_k_pool, const void* idx_k_scale,
+                            const int32_t* block_table,
                             const int32_t* ctx_lens, const int32_t* rows, int32_t nrows,
                             double* scores) {
   int T = p->query_len, H = p->num_idx_heads, E = p->idx_dim, BS = p->block_size;
@@ -187,7 +199,7 @@ int msa_oracle_index_scores(const oracle_problem* p, const uint16_t* idx_q,
         for (int h = 0; h < H; h++)
           for (int d = 0; d < E; d++)
             s += msa_oracle_bf16_to_double(idx_q[((int64_t)r * H + h) * E + d]) *
-                 idx_key_value(p, idx_k_pool, phys, h, tok, d);
+                 idx_key_value(p, idx_k_pool, idx_k_scale, phys, h, tok, d);
         if (s > best) best = s;
       }
       out[c] = best;

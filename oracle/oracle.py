@@ -23,7 +23,7 @@ _SRC = os.path.join(_HERE, "msa_oracle.c")
 _LIB = os.path.join(_HERE, "libmsa_oracle.so")
 
 KV_DTYPES = {"bf16": 0, "fp8": 1, "nvfp4": 2}
-IDX_DTYPES = {"bf16": 0, "fp8": 1}
+IDX_DTYPES = {"bf16": 0, "fp8": 1, "nvfp4": 2}
 
 
 def build(force: bool = False) -> str:
@@ -96,7 +96,7 @@ def lib():
         L.msa_oracle_e4m3_to_double.argtypes = [ctypes.c_uint8]
         L.msa_oracle_e2m1_to_double.restype = ctypes.c_double
         L.msa_oracle_e2m1_to_double.argtypes = [ctypes.c_uint8]
-        L.msa_oracle_index_scores.argtypes = [pp, vp, vp, vp, vp, vp, ctypes.c_int32, vp]
+        L.msa_oracle_index_scores.argtypes = [pp, vp, vp, vp, vp, vp, vp, ctypes.c_int32, vp]
         L.msa_oracle_select.argtypes = [pp, vp, vp, vp, ctypes.c_int32, vp, vp]
         L.msa_oracle_page_table.argtypes = [pp, vp, vp, vp, ctypes.c_int32, vp]
         L.msa_oracle_attention.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
@@ -135,17 +135,27 @@ def e2m1_to_double(nibble: int) -> float:
     return lib().msa_oracle_e2m1_to_double(nibble)
 
 
-def index_scores(prob, idx_q, idx_k_pool, block_table, ctx_lens, rows=None):
-    """Block scores [nrows, max_blocks] (float64, -inf past the local block)."""
+def index_scores(prob, idx_q, idx_k_pool, block_table, ctx_lens, rows=None, *,
+                 idx_k_scale=None):
+    """Block scores [nrows, max_blocks] (float64, -inf past the local block).
+    4-bit index keys (idx_dtype "nvfp4") need `idx_k_scale`, the E4M3 code of
+    every group of 16 dims."""
     rows, n = _rows(prob, rows)
     idx_q = _c(idx_q, np.uint16)
     idx_k_pool = _c(idx_k_pool, np.uint16 if prob.idx_dtype == "bf16" else np.uint8)
+    if prob.idx_dtype == "nvfp4":
+        if idx_k_scale is None:
+            raise ValueError("4-bit index keys need idx_k_scale")
+        idx_k_scale = _c(idx_k_scale, np.uint8)
+    else:
+        idx_k_scale = None
     block_table = _c(block_table, np.int32)
     ctx_lens = _c(ctx_lens, np.int32)
     out = np.empty((n, prob.max_blocks), dtype=np.float64)
     p = prob.c()
     lib().msa_oracle_index_scores(ctypes.byref(p), _ptr(idx_q), _ptr(idx_k_pool),
-                                  _ptr(block_table), _ptr(ctx_lens), _ptr(rows), n, _ptr(out))
+                                  _ptr(idx_k_scale), _ptr(block_table), _ptr(ctx_lens),
+                                  _ptr(rows), n, _ptr(out))
     return out
 
 
@@ -198,10 +208,11 @@ def attention(prob, q, k_pool, v_pool, k_scale, v_scale, block_table, ctx_lens, 
 
 
 def decode(prob, q, idx_q, k_pool, v_pool, k_scale, v_scale, idx_k_pool, block_table,
-           ctx_lens, rows=None):
+           ctx_lens, rows=None, *, idx_k_scale=None):
     """The whole path for the given rows: dict of scores, selected, n_selected,
     page_table and out."""
-    s = index_scores(prob, idx_q, idx_k_pool, block_table, ctx_lens, rows)
+    s = index_scores(prob, idx_q, idx_k_pool, block_table, ctx_lens, rows,
+                     idx_k_scale=idx_k_scale)
     sel, nsel = select(prob, s, ctx_lens, rows)
     pt = page_table(prob, sel, block_table, rows)
     out = attention(prob, q, k_pool, v_pool, k_scale, v_scale, block_table, ctx_lens, sel, rows)

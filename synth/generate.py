@@ -39,7 +39,12 @@ IDX_DIM = 64
 CHUNK = 1 << 24  # elements generated per tensor op batch (bounds temporaries)
 
 # stream ids: one per generated quantity
-_S_CTX, _S_PERM, _S_PLANT, _S_IQ, _S_IK, _S_Q, _S_K, _S_V = range(1, 9)
+_S_CTX, _S_PERM, _S_PLANT, _S_IQ, _S_IK, _S_Q, _S_K, _S_V, _S_IKS = range(1, 10)
+
+# E4M3 codes of the 4-bit index-key scales the generator draws: 1, 2, 4, 8.
+# With E2M1 codes (multiples of 0.5, at most 6) and integer queries in
+# [-8, 8], every product and every fp32 partial sum of a score is exact.
+IDX_FP4_SCALE_CODES = (0x38, 0x40, 0x48, 0x50)
 
 
 # ---------------------------------------------------------------- hashing
@@ -103,6 +108,12 @@ def _small_ints(seed: int, stream: int, start: int, n: int, device, lo=-8, hi=8)
     return (r % (hi - lo + 1) + lo).to(torch.float32)
 
 
+def _uniform_codes(seed: int, stream: int, start: int, n: int, device, count: int):
+    """n integers uniform in [0, count) for a power-of-two count (float32)."""
+    idx = torch.arange(start, start + n, dtype=torch.int64, device=device)
+    return (rand32(seed, stream, idx) & (count - 1)).to(torch.float32)
+
+
 def _randint_host(seed: int, stream: int, idx: np.ndarray) -> np.ndarray:
     return rand32(seed, stream, torch.from_numpy(np.asarray(idx, dtype=np.int64))).numpy()
 
@@ -161,7 +172,7 @@ class MSAConfig:
     ctx_lo: int
     ctx_hi: int
     kv_dtype: str = "bf16"      # bf16 | fp8 | nvfp4
-    idx_dtype: str = "bf16"     # bf16 | fp8
+    idx_dtype: str = "bf16"     # bf16 | fp8 | nvfp4
     n_plant: int = 0
     permute: bool = True
     seed: int = 1000
@@ -292,11 +303,17 @@ def make_workload(cfg: MSAConfig, device="cpu", layer: int = 0) -> Workload:
     _fill(iq, lambda s, n: _small_ints(seed, _S_IQ, s, n, device))
     t["idx_q"] = iq.to(torch.bfloat16)
 
-    # index keys: integers in [-8, 8], by physical element position
+    # index keys, by physical element position: integers in [-8, 8] (bf16 /
+    # fp8), or 4-bit E2M1 codes with an E4M3 scale per 16 dims (nvfp4)
+    fp4 = cfg.idx_dtype == "nvfp4"
     ik = torch.empty((NB, cfg.num_idx_heads, BLOCK, IDX_DIM), dtype=torch.int8, device=device)
-    _fill(ik, lambda s, n: _small_ints(seed, _S_IK, s, n, device))
+    if fp4:
+        _fill(ik, lambda s, n: _uniform_codes(seed, _S_IK, s, n, device, 16))
+    else:
+        _fill(ik, lambda s, n: _small_ints(seed, _S_IK, s, n, device))
 
-    # planted blocks: +4 on the components aligned with sign(index q of row 0)
+    # planted blocks: components aligned with sign(index q of row 0) get +4
+    # (integer keys) or the E2M1 code of +-6 (4-bit keys)
     planted: List[List[int]] = []
     for b in range(B):
         local0 = (ctx[b] - T) // BLOCK
@@ -312,9 +329,23 @@ def make_workload(cfg: MSAConfig, device="cpu", layer: int = 0) -> Workload:
             sgn = torch.sign(iq[b * T]).to(torch.int8)  # [Hidx, 64]
             pb = torch.tensor([int(bt[b, c]) for c in chosen], dtype=torch.int64,
                               device=device)
-            ik[pb] += 4 * sgn.unsqueeze(1)
+            if fp4:
+                six = torch.where(sgn > 0, 0x7, 0xF).to(torch.int8)  # +6 / -6
+                blk = ik[pb]
+                ik[pb] = torch.where(sgn.unsqueeze(1) != 0, six.unsqueeze(1), blk)
+            else:
+                ik[pb] += 4 * sgn.unsqueeze(1)
         planted.append(chosen)
-    if cfg.idx_dtype == "bf16":
+    t["idx_k_scale"] = None
+    if fp4:
+        nib = ik.to(torch.uint8).view(NB, cfg.num_idx_heads, BLOCK, IDX_DIM // 2, 2)
+        t["idx_k_pool"] = (nib[..., 0] | (nib[..., 1] << 4)).contiguous()
+        sc = torch.empty((NB, cfg.num_idx_heads, BLOCK, IDX_DIM // 16), dtype=torch.int8,
+                         device=device)
+        _fill(sc, lambda s, n: _uniform_codes(seed, _S_IKS, s, n, device, 4))
+        codes = torch.tensor(IDX_FP4_SCALE_CODES, dtype=torch.uint8, device=device)
+        t["idx_k_scale"] = codes[sc.to(torch.int64)]
+    elif cfg.idx_dtype == "bf16":
         t["idx_k_pool"] = ik.to(torch.bfloat16)
     else:
         t["idx_k_pool"] = ik.to(torch.float32).to(torch.float8_e4m3fn).view(torch.uint8)

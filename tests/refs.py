@@ -48,7 +48,11 @@ def decode_kv(kind: str, pool: np.ndarray, scale) -> np.ndarray:
     return vals * np.repeat(s, 16, axis=-1)
 
 
-def decode_idx(kind: str, pool: np.ndarray) -> np.ndarray:
+def decode_idx(kind: str, pool: np.ndarray, scale=None) -> np.ndarray:
+    """Dense float64 index keys [NB, Hidx, 128, 64]; 4-bit keys use the same
+    packing and per-16 E4M3 scales as 4-bit K / V."""
+    if kind == "nvfp4":
+        return decode_kv("nvfp4", pool, scale)
     return decode_bf16(pool) if kind == "bf16" else decode_e4m3(pool)
 
 
@@ -65,7 +69,8 @@ def token_scores(cfg, h, b, t) -> np.ndarray:
     nblk = -(-L // 128)
     T = cfg.query_len
     p = L - T + t
-    ik = logical(decode_idx(cfg.idx_dtype, h["idx_k_pool"]), h["block_table"][b], nblk, L)
+    ik = logical(decode_idx(cfg.idx_dtype, h["idx_k_pool"], h.get("idx_k_scale")),
+                 h["block_table"][b], nblk, L)
     iq = decode_bf16(h["idx_q"][b * T + t])               # [Hidx, 64]
     s = np.einsum("hd,hld->l", iq, ik)                     # sum over heads and dims
     return s[:p + 1]

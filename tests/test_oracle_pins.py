@@ -27,7 +27,8 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_figures.json")
 def run_oracle(cfg, h, sm_scale=0.0, rows=None):
     P = problem_of(cfg, sm_scale)
     return oracle.decode(P, h["q"], h["idx_q"], h["k_pool"], h["v_pool"], h["k_scale"],
-                         h["v_scale"], h["idx_k_pool"], h["block_table"], h["ctx_lens"], rows)
+                         h["v_scale"], h["idx_k_pool"], h["block_table"], h["ctx_lens"], rows,
+                         idx_k_scale=h.get("idx_k_scale"))
 
 
 def positions(cfg, h):
@@ -73,13 +74,15 @@ def test_e2m1_decoder_matches_ocp_table():
     dict(query_len=3, num_idx_heads=3, ctx_lo=300, ctx_hi=1100, batch=3),
     dict(idx_dtype="fp8", num_idx_heads=2, ctx_lo=129, ctx_hi=700, batch=3, query_len=2),
     dict(ctx_list=(1, 127, 128, 129), batch=4, query_len=1),
+    dict(idx_dtype="nvfp4", num_idx_heads=2, ctx_lo=129, ctx_hi=900, batch=3, query_len=2,
+         n_plant=2),
 ])
 def test_block_scores_brute_force(kw):
     cfg = small_config(**kw)
     w = make_workload(cfg)
     h = host_arrays(w)
     s = oracle.index_scores(problem_of(cfg), h["idx_q"], h["idx_k_pool"], h["block_table"],
-                            h["ctx_lens"])
+                            h["ctx_lens"], idx_k_scale=h["idx_k_scale"])
     for b, t, r, p in positions(cfg, h):
         ts = token_scores(cfg, h, b, t)
         local = p // 128
@@ -105,6 +108,41 @@ def test_block_score_sums_heads_before_max():
     s = oracle.index_scores(problem_of(cfg), h["idx_q"], h["idx_k_pool"], h["block_table"],
                             h["ctx_lens"])
     assert s[0, 0] == 64.0  # not 128
+
+
+def test_fp4_index_key_closed_form():
+    """4-bit index keys: E2M1 code 0x2 (1.0) times E4M3 scale 0x40 (2.0) in
+    every dim, a query of ones: each token scores 64 * 2 per head; one dim
+    recoded to -6 (0xF) under scale 8 (0x50) drops a token by 2 + 48."""
+    cfg = small_config(batch=1, ctx_list=(128,), num_idx_heads=2, idx_dtype="nvfp4")
+    w = make_workload(cfg)
+    h = host_arrays(w)
+    ik = np.full_like(h["idx_k_pool"], 0x22)      # two 1.0 codes per byte
+    sc = np.full_like(h["idx_k_scale"], 0x40)     # 2.0
+    iq = np.full_like(h["idx_q"], np.uint16(0x3F80))
+    s = oracle.index_scores(problem_of(cfg), iq, ik, h["block_table"], h["ctx_lens"],
+                            idx_k_scale=sc)
+    assert s[0, 0] == 2 * 64 * 2.0
+    phys = int(h["block_table"][0, 0])
+    ik[phys, :, :, 0] = 0xF2    # dim 1 of every token and head: -6
+    sc[phys, :, :, 0] = 0x50    # dims 0..15 scaled by 8
+    s = oracle.index_scores(problem_of(cfg), iq, ik, h["block_table"], h["ctx_lens"],
+                            idx_k_scale=sc)
+    # per head: 15 dims of 1 * 8, one of -6 * 8, 48 dims of 1 * 2
+    assert s[0, 0] == 2 * (15 * 8 - 48 + 48 * 2)
+    with pytest.raises(ValueError):
+        oracle.index_scores(problem_of(cfg), iq, ik, h["block_table"], h["ctx_lens"])
+
+
+def test_fp4_index_keys_select_planted_blocks():
+    cfg = small_config(batch=3, ctx_lo=6000, ctx_hi=9000, num_idx_heads=2, idx_dtype="nvfp4",
+                       n_plant=6, seed=31)
+    w = make_workload(cfg)
+    h = host_arrays(w)
+    res = run_oracle(cfg, h)
+    for b in range(cfg.batch):
+        sel = set(int(x) for x in res["selected"][b] if x >= 0)
+        assert set(w.planted[b]) <= sel, (b, w.planted[b], sel)
 
 
 # --------------------------------------------------------------- selection
