@@ -39,8 +39,9 @@ def algorithmic_bytes(w, selected):
     is the [R, topk] selection of one run."""
     c = w.cfg
     T = c.query_len
-    idx_elem = 2 if c.idx_dtype == "bf16" else 1
-    idx = sum(w.nblk) * 128 * c.num_idx_heads * 64 * idx_elem
+    # index key bytes per (token, head): bf16 128, fp8 64, 4-bit 32 + 4 scales
+    per_tok = {"bf16": 128, "fp8": 64, "nvfp4": 36}[c.idx_dtype]
+    idx = sum(w.nblk) * 128 * c.num_idx_heads * per_tok
     # per attended key and KV head: K and V rows plus their scales
     per_key = 2 * 128 * kv_elem_bytes(c.kv_dtype)
     if c.kv_dtype == "fp8":
@@ -124,6 +125,7 @@ def cpu_baseline(w, n_requests, min_seconds=10.0):
                           device=t["q"].device)
     iq = host(t["idx_q"][rows_q])
     ik = host(t["idx_k_pool"][phys])
+    iks = None if t.get("idx_k_scale") is None else host(t["idx_k_scale"][phys])
     q = host(t["q"][rows_q])
 
     def kv_of_selected(sel):
@@ -144,7 +146,7 @@ def cpu_baseline(w, n_requests, min_seconds=10.0):
     elapsed, passes, kv = 0.0, 0, None
     while passes == 0 or elapsed < min_seconds:
         t0 = time.perf_counter()
-        s = oracle.index_scores(P, iq, ik, bt, ctx)
+        s = oracle.index_scores(P, iq, ik, bt, ctx, idx_k_scale=iks)
         sel, _ = oracle.select(P, s, ctx)
         oracle.page_table(P, sel, bt)
         t1 = time.perf_counter()
@@ -198,7 +200,8 @@ def main():
     wt = w.tensors
     p, t = msa.describe(wt["q"], wt["idx_q"], wt["k_pool"], wt["v_pool"], wt["k_scale"],
                         wt["v_scale"], wt["idx_k_pool"], wt["block_table"], wt["ctx_lens"],
-                        decode_query_len=cfg.query_len, topk=cfg.topk)
+                        decode_query_len=cfg.query_len, topk=cfg.topk,
+                        idx_k_scale=wt.get("idx_k_scale"))
     R = cfg.rows
     o = {
         "scores": torch.empty((R, cfg.max_blocks), dtype=torch.float32, device="cuda"),

@@ -64,7 +64,7 @@ class Problem(ctypes.Structure):
 class Tensors(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("q", "idx_q", "k_pool", "v_pool", "k_scale", "v_scale", "idx_k_pool",
-                 "block_table", "ctx_lens")]
+                 "block_table", "ctx_lens", "idx_k_scale")]
 
 
 def _load():
@@ -121,16 +121,17 @@ def _p(t: Optional[torch.Tensor]):
 
 
 def tensors(q=None, idx_q=None, k_pool=None, v_pool=None, k_scale=None, v_scale=None,
-            idx_k_pool=None, block_table=None, ctx_lens=None) -> Tensors:
+            idx_k_pool=None, block_table=None, ctx_lens=None, idx_k_scale=None) -> Tensors:
     return Tensors(*(None if t is None else t.data_ptr() for t in
                      (q, idx_q, k_pool, v_pool, k_scale, v_scale, idx_k_pool, block_table,
-                      ctx_lens)))
+                      ctx_lens, idx_k_scale)))
 
 
 def describe(q, idx_q, k_pool, v_pool, k_scale, v_scale, idx_k_pool, block_table, ctx_lens,
-             decode_query_len=1, topk=16, sm_scale=0.0):
+             decode_query_len=1, topk=16, sm_scale=0.0, idx_k_scale=None):
     """(Problem, Tensors) for device tensors in the boundary's layouts; the
-    dimensions and dtypes are read from the tensor shapes."""
+    dimensions and dtypes are read from the tensor shapes (index keys with an
+    idx_k_scale pool are 4-bit)."""
     B = int(ctx_lens.shape[0])
     if k_pool.dtype == torch.bfloat16:
         kv = "bf16"
@@ -138,11 +139,15 @@ def describe(q, idx_q, k_pool, v_pool, k_scale, v_scale, idx_k_pool, block_table
         kv = "fp8"
     else:
         kv = "nvfp4"
+    if idx_k_pool.dtype == torch.bfloat16:
+        idx = "bf16"
+    else:
+        idx = "nvfp4" if idx_k_scale is not None else "fp8"
     p = problem(B, decode_query_len, int(q.shape[1]), int(k_pool.shape[1]),
                 int(idx_k_pool.shape[1]), int(block_table.shape[1]), int(k_pool.shape[0]),
-                kv_dtype=kv, idx_k_dtype="bf16" if idx_k_pool.dtype == torch.bfloat16 else "fp8",
-                topk=topk, sm_scale=sm_scale)
-    t = tensors(q, idx_q, k_pool, v_pool, k_scale, v_scale, idx_k_pool, block_table, ctx_lens)
+                kv_dtype=kv, idx_k_dtype=idx, topk=topk, sm_scale=sm_scale)
+    t = tensors(q, idx_q, k_pool, v_pool, k_scale, v_scale, idx_k_pool, block_table, ctx_lens,
+                idx_k_scale)
     return p, t
 
 

@@ -55,7 +55,7 @@ int check_problem(const msa_problem* p, Dims* d) {
       p->num_idx_heads > 16 || p->num_q_heads / p->num_kv_heads > 16)
     return MSA_ERR_UNSUPPORTED;
   if (p->kv_dtype < MSA_DTYPE_BF16 || p->kv_dtype > MSA_DTYPE_NVFP4) return MSA_ERR_UNSUPPORTED;
-  if (p->idx_k_dtype != MSA_DTYPE_BF16 && p->idx_k_dtype != MSA_DTYPE_FP8_E4M3)
+  if (p->idx_k_dtype < MSA_DTYPE_BF16 || p->idx_k_dtype > MSA_DTYPE_NVFP4)
     return MSA_ERR_UNSUPPORTED;
   // grid limits: one wave per (request, block) in the scan
   if ((long)p->batch * p->max_blocks_per_seq > (1L << 30) ||
@@ -81,12 +81,13 @@ int check_ptr(const void* p) {
   return aligned16(p) ? MSA_OK : MSA_ERR_INVALID_ARG;
 }
 
-int check_index_inputs(const msa_tensors* t) {
+int check_index_inputs(const Dims& d, const msa_tensors* t) {
   if (!t) return MSA_ERR_INVALID_ARG;
   int e;
   if ((e = check_ptr(t->idx_q)) || (e = check_ptr(t->idx_k_pool)) ||
       (e = check_ptr(t->block_table)) || (e = check_ptr(t->ctx_lens)))
     return e;
+  if (d.idx_dtype == MSA_DTYPE_NVFP4 && (e = check_ptr(t->idx_k_scale))) return e;
   return MSA_OK;
 }
 
@@ -120,10 +121,10 @@ int msa_index_score(const msa_problem* p, const msa_tensors* t, float* block_sco
   Dims d;
   int e;
   if ((e = check_problem(p, &d))) return e;
-  if ((e = check_index_inputs(t)) || (e = check_ptr(block_scores))) return e;
+  if ((e = check_index_inputs(d, t)) || (e = check_ptr(block_scores))) return e;
   std::string note;
-  e = hip_status(launch_index_scan(d, t->idx_q, t->idx_k_pool, t->block_table, t->ctx_lens,
-                                   block_scores, (hipStream_t)stream, &note));
+  e = hip_status(launch_index_scan(d, t->idx_q, t->idx_k_pool, t->idx_k_scale, t->block_table,
+                                   t->ctx_lens, block_scores, (hipStream_t)stream, &note));
   if (e == MSA_OK) g_last_dispatch = note;
   return e;
 }
@@ -190,7 +191,7 @@ int msa_decode(const msa_problem* p, const msa_tensors* t, int32_t* selected,
   Dims d;
   int e;
   if ((e = check_problem(p, &d))) return e;
-  if ((e = check_index_inputs(t)) || (e = check_kv_inputs(d, t)) || (e = check_ptr(out)) ||
+  if ((e = check_index_inputs(d, t)) || (e = check_kv_inputs(d, t)) || (e = check_ptr(out)) ||
       (e = check_ptr(workspace)))
     return e;
   if ((selected && !aligned16(selected)) || (page_table && !aligned16(page_table)))
@@ -204,8 +205,8 @@ int msa_decode(const msa_problem* p, const msa_tensors* t, int32_t* selected,
   int32_t* pt = page_table ? page_table : reinterpret_cast<int32_t*>(ws + w.page_table);
   hipStream_t s = (hipStream_t)stream;
   std::string note;
-  if ((e = hip_status(launch_index_scan(d, t->idx_q, t->idx_k_pool, t->block_table, t->ctx_lens,
-                                        scores, s, &note))))
+  if ((e = hip_status(launch_index_scan(d, t->idx_q, t->idx_k_pool, t->idx_k_scale,
+                                        t->block_table, t->ctx_lens, scores, s, &note))))
     return e;
   note += " ";
   if ((e = hip_status(launch_select(d, scores, t->ctx_lens, t->block_table, sel, nsel, pt, s,

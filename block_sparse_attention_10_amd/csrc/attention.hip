@@ -486,8 +486,14 @@ __global__ void selftest_kernel(float* out) {
     out[i] = e2m1x2_to_f32x2((uint32_t)(i - 256), 0).x;
   } else if (i < 256 + 32) {
     out[i] = e2m1x2_to_f32x2((uint32_t)(i - 272) << 4, 0).y;
-  } else if (i < 256 + 32 + 256) {
+  } else if (i < 544) {
     out[i] = e4m3_to_f32((uint32_t)(i - 288));
+  } else if (i < 560) {
+    out[i] = bf16_bits_to_f32(e2m1x2_to_bf16x2<0>((uint32_t)(i - 544)) & 0xFFFFu);
+  } else if (i < 576) {
+    out[i] = bf16_bits_to_f32(e2m1x2_to_bf16x2<0>((uint32_t)(i - 560) << 4) >> 16);
+  } else if (i < 832) {
+    out[i] = e4m3x2_to_f32x2((uint32_t)(i - 576) << 8).y;
   }
 }
 
@@ -582,7 +588,7 @@ hipError_t launch_sparse_attention(const Dims& d, const void* q, const void* k_p
 }
 
 hipError_t launch_selftest_decoders(float* out, hipStream_t s) {
-  hipLaunchKernelGGL(selftest_kernel, dim3(3), dim3(256), 0, s, out);
+  hipLaunchKernelGGL(selftest_kernel, dim3(4), dim3(256), 0, s, out);
   return hipGetLastError();
 }
 

@@ -11,10 +11,15 @@
 // so it runs on the VALU.  One wave scores one logical block for all rows of
 // its request: every load instruction moves 1 KB of contiguous keys (64
 // lanes x 16 B); bf16 keys feed v_dot2_f32_bf16 directly, fp8 keys are
-// widened to bf16 pairs in registers first.  Index queries and keys hold
-// small integers, so every fp32 partial sum is exact in any order.  The lanes
-// that share a token are folded by a transpose-reduce (each butterfly stage
-// halves the partials a lane carries), then the wave takes the causal max.
+// widened to bf16 pairs in registers first.  4-bit keys (E2M1 codes, one
+// E4M3 scale per 16 dims, the NVFP4 layout of the aisoku.org article,
+// section "何が新しいか") are widened to unscaled bf16 pairs, dotted with the
+// query per group of 16 dims, and each group sum is multiplied by its
+// scale.  With the synthetic keys (small integers, or E2M1 codes under
+// power-of-two scales) every fp32 partial sum is exact in any order.  The
+// lanes that share a token are folded by a transpose-reduce (each butterfly
+// stage halves the partials a lane carries), then the wave takes the causal
+// max.
 #include "msa_device.h"
 #include "msa_internal.h"
 
@@ -40,26 +45,36 @@ __device__ __forceinline__ void fold_stage(float* v, int lane) {
   }
 }
 
+// Key formats of the index cache.
+enum KeyKind { kBf16 = 0, kFp8 = 1, kFp4 = 2 };
+
 // Scores of logical block c (a real block: c * 128 < L) for every row of
-// request b, written by lane 0.  KB: bytes per key element (2 = bf16, 1 =
-// fp8 e4m3).  TR: rows scored per pass (1, 2 or 4); more rows loop.
-template <int KB, int TR>
+// request b, written by lane 0.  TR: rows scored per pass (1, 2 or 4); more
+// rows loop.  idx_ks: the 4-bit keys' scale pool (unused otherwise).
+template <int KIND, int TR>
 __device__ __forceinline__ void scan_block(const uint16_t* __restrict__ idx_q,
                                            const uint8_t* __restrict__ idx_k,
+                                           const uint8_t* __restrict__ idx_ks,
                                            const int32_t* __restrict__ block_table,
                                            float* __restrict__ scores, int b, int c, int L, int T,
                                            int Hidx, int MAXB, int lane) {
-  constexpr int DPL = 16 / KB;       // dims per lane per load (8 / 16)
-  constexpr int LPT = kIdxDim / DPL; // lanes per token (8 / 4)
-  constexpr int TPL = kWave / LPT;   // tokens per load instruction (8 / 16)
-  constexpr int NLD = kBlock / TPL;  // loads per (block, head) (16 / 8)
-  constexpr int QW = DPL / 2;        // query dwords per lane per row (4 / 8)
+  constexpr int DPL = KIND == kBf16 ? 8 : (KIND == kFp8 ? 16 : 32);  // dims per lane per load
+  constexpr int LPT = kIdxDim / DPL; // lanes per token (8 / 4 / 2)
+  constexpr int TPL = kWave / LPT;   // tokens per load instruction (8 / 16 / 32)
+  constexpr int NLD = kBlock / TPL;  // loads per (block, head) (16 / 8 / 4)
+  constexpr int QW = DPL / 2;        // query dwords per lane per row (4 / 8 / 16)
   static_assert(NLD == 2 * LPT, "transpose-reduce leaves two tokens per lane");
 
   float* srow = scores + (size_t)b * T * MAXB + c;
-  const size_t head_bytes = (size_t)kBlock * kIdxDim * KB;
-  const uint8_t* kblk =
-      idx_k + (size_t)block_table[(size_t)b * MAXB + c] * Hidx * head_bytes + lane * 16;
+  // bytes of one (block, head): LPT lane slices of 16 B per token
+  const size_t head_bytes = (size_t)kBlock * LPT * 16;
+  const size_t phys = (size_t)block_table[(size_t)b * MAXB + c];
+  const uint8_t* kblk = idx_k + phys * Hidx * head_bytes + lane * 16;
+  // 4-bit scales [block][head][token][4]: this lane's two codes (its 32
+  // dims) of token 32 i + lane / 2 sit at sblk + i * 128
+  const uint8_t* sblk = nullptr;
+  if constexpr (KIND == kFp4)
+    sblk = idx_ks + phys * Hidx * (kBlock * 4) + (lane >> 1) * 4 + (lane & 1) * 2;
   const int dim0 = (lane % LPT) * DPL;
 
   for (int t0 = 0; t0 < T; t0 += TR) {
@@ -71,9 +86,16 @@ __device__ __forceinline__ void scan_block(const uint16_t* __restrict__ idx_q,
 
     for (int h = 0; h < Hidx; ++h) {
       u32x4 kv[NLD];
+      uint32_t ks[NLD];
       const uint8_t* kh = kblk + (size_t)h * head_bytes;
 #pragma unroll
       for (int i = 0; i < NLD; ++i) kv[i] = ldg128_stream(kh + i * 1024);
+      if constexpr (KIND == kFp4) {
+        const uint8_t* sh = sblk + (size_t)h * (kBlock * 4);
+#pragma unroll
+        for (int i = 0; i < NLD; ++i)
+          ks[i] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(sh + i * 128));
+      }
       uint32_t qv[TR][QW];
 #pragma unroll
       for (int t = 0; t < TR; ++t) {
@@ -88,22 +110,45 @@ __device__ __forceinline__ void scan_block(const uint16_t* __restrict__ idx_q,
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
         uint32_t kw[QW];
-        if constexpr (KB == 2) {
-          kw[0] = kv[i].x; kw[1] = kv[i].y; kw[2] = kv[i].z; kw[3] = kv[i].w;
-        } else {
-          const uint32_t src[4] = {kv[i].x, kv[i].y, kv[i].z, kv[i].w};
+        const uint32_t src[4] = {kv[i].x, kv[i].y, kv[i].z, kv[i].w};
+        if constexpr (KIND == kBf16) {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) kw[w] = src[w];
+        } else if constexpr (KIND == kFp8) {
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
             kw[2 * w] = e4m3x2_to_bf16x2<false>(src[w]);
             kw[2 * w + 1] = e4m3x2_to_bf16x2<true>(src[w]);
           }
+        } else {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            kw[4 * w] = e2m1x2_to_bf16x2<0>(src[w]);
+            kw[4 * w + 1] = e2m1x2_to_bf16x2<1>(src[w]);
+            kw[4 * w + 2] = e2m1x2_to_bf16x2<2>(src[w]);
+            kw[4 * w + 3] = e2m1x2_to_bf16x2<3>(src[w]);
+          }
         }
+        if constexpr (KIND == kFp4) {
+          // dims 0..15 of the lane under scale 0, 16..31 under scale 1
+          const f32x2 sc = e4m3x2_to_f32x2(ks[i]);
 #pragma unroll
-        for (int t = 0; t < TR; ++t) {
-          float acc = part[t][i];
+          for (int t = 0; t < TR; ++t) {
+            float g0 = 0.f, g1 = 0.f;
 #pragma unroll
-          for (int w = 0; w < QW; ++w) acc = dot2_bf16(kw[w], qv[t][w], acc);
-          part[t][i] = acc;
+            for (int w = 0; w < QW / 2; ++w) g0 = dot2_bf16(kw[w], qv[t][w], g0);
+#pragma unroll
+            for (int w = QW / 2; w < QW; ++w) g1 = dot2_bf16(kw[w], qv[t][w], g1);
+            part[t][i] = fmaf(sc.y, g1, fmaf(sc.x, g0, part[t][i]));
+          }
+        } else {
+#pragma unroll
+          for (int t = 0; t < TR; ++t) {
+            float acc = part[t][i];
+#pragma unroll
+            for (int w = 0; w < QW; ++w) acc = dot2_bf16(kw[w], qv[t][w], acc);
+            part[t][i] = acc;
+          }
         }
       }
     }
@@ -116,8 +161,10 @@ __device__ __forceinline__ void scan_block(const uint16_t* __restrict__ idx_q,
         fold_stage<8, 4>(v, lane);
         fold_stage<4, 2>(v, lane);
         fold_stage<2, 1>(v, lane);
-      } else {
+      } else if constexpr (LPT == 4) {
         fold_stage<4, 2>(v, lane);
+        fold_stage<2, 1>(v, lane);
+      } else {
         fold_stage<2, 1>(v, lane);
       }
       // lane now holds the full scores of loads i = 2 * (lane % LPT) + e
@@ -136,11 +183,12 @@ __device__ __forceinline__ void scan_block(const uint16_t* __restrict__ idx_q,
 
 // msa_index_score: one wave per (request, logical block); blocks past the
 // context score -inf for every row.
-template <int KB, int TR>
+template <int KIND, int TR>
 __global__ __launch_bounds__(256) void index_scan_kernel(
     const uint16_t* __restrict__ idx_q, const uint8_t* __restrict__ idx_k,
-    const int32_t* __restrict__ block_table, const int32_t* __restrict__ ctx_lens,
-    float* __restrict__ scores, int B, int T, int Hidx, int MAXB) {
+    const uint8_t* __restrict__ idx_ks, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ ctx_lens, float* __restrict__ scores, int B, int T, int Hidx,
+    int MAXB) {
   const int lane = lane_id();
   const int item = blockIdx.x * 4 + wave_id();
   if (item >= B * MAXB) return;
@@ -152,40 +200,46 @@ __global__ __launch_bounds__(256) void index_scan_kernel(
     for (int t = lane; t < T; t += kWave) srow[(size_t)t * MAXB] = -INFINITY;
     return;
   }
-  scan_block<KB, TR>(idx_q, idx_k, block_table, scores, b, c, L, T, Hidx, MAXB, lane);
+  scan_block<KIND, TR>(idx_q, idx_k, idx_ks, block_table, scores, b, c, L, T, Hidx, MAXB, lane);
 }
 
-template <int KB>
-hipError_t launch_kb(const Dims& d, const void* idx_q, const void* idx_k, const int32_t* bt,
-                     const int32_t* cl, float* scores, hipStream_t s, std::string* note) {
+template <int KIND>
+hipError_t launch_kind(const Dims& d, const void* idx_q, const void* idx_k, const void* idx_ks,
+                       const int32_t* bt, const int32_t* cl, float* scores, hipStream_t s,
+                       std::string* note) {
   const long items = (long)d.B * d.MAXB;
   const dim3 grid((unsigned)((items + 3) / 4)), block(256);
   const auto* q = static_cast<const uint16_t*>(idx_q);
   const auto* k = static_cast<const uint8_t*>(idx_k);
+  const auto* ks = static_cast<const uint8_t*>(idx_ks);
   const int tr = d.T == 1 ? 1 : (d.T == 2 ? 2 : 4);
   if (tr == 1)
-    hipLaunchKernelGGL((index_scan_kernel<KB, 1>), grid, block, 0, s, q, k, bt, cl, scores, d.B,
-                       d.T, d.Hidx, d.MAXB);
+    hipLaunchKernelGGL((index_scan_kernel<KIND, 1>), grid, block, 0, s, q, k, ks, bt, cl, scores,
+                       d.B, d.T, d.Hidx, d.MAXB);
   else if (tr == 2)
-    hipLaunchKernelGGL((index_scan_kernel<KB, 2>), grid, block, 0, s, q, k, bt, cl, scores, d.B,
-                       d.T, d.Hidx, d.MAXB);
+    hipLaunchKernelGGL((index_scan_kernel<KIND, 2>), grid, block, 0, s, q, k, ks, bt, cl, scores,
+                       d.B, d.T, d.Hidx, d.MAXB);
   else
-    hipLaunchKernelGGL((index_scan_kernel<KB, 4>), grid, block, 0, s, q, k, bt, cl, scores, d.B,
-                       d.T, d.Hidx, d.MAXB);
+    hipLaunchKernelGGL((index_scan_kernel<KIND, 4>), grid, block, 0, s, q, k, ks, bt, cl, scores,
+                       d.B, d.T, d.Hidx, d.MAXB);
+  static const char* names[3] = {"bf16", "fp8", "nvfp4"};
   if (note)
-    *note += std::string("index_scan<") + (KB == 2 ? "bf16" : "fp8") + ",rows" +
-             std::to_string(tr) + ">[grid=" + std::to_string(grid.x) + "x256]";
+    *note += std::string("index_scan<") + names[KIND] + ",rows" + std::to_string(tr) +
+             ">[grid=" + std::to_string(grid.x) + "x256]";
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_index_scan(const Dims& d, const void* idx_q, const void* idx_k,
-                             const int32_t* block_table, const int32_t* ctx_lens,
-                             float* scores, hipStream_t s, std::string* note) {
-  if (d.idx_dtype == 0)
-    return launch_kb<2>(d, idx_q, idx_k, block_table, ctx_lens, scores, s, note);
-  return launch_kb<1>(d, idx_q, idx_k, block_table, ctx_lens, scores, s, note);
+                             const void* idx_k_scale, const int32_t* block_table,
+                             const int32_t* ctx_lens, float* scores, hipStream_t s,
+                             std::string* note) {
+  if (d.idx_dtype == kBf16)
+    return launch_kind<kBf16>(d, idx_q, idx_k, nullptr, block_table, ctx_lens, scores, s, note);
+  if (d.idx_dtype == kFp8)
+    return launch_kind<kFp8>(d, idx_q, idx_k, nullptr, block_table, ctx_lens, scores, s, note);
+  return launch_kind<kFp4>(d, idx_q, idx_k, idx_k_scale, block_table, ctx_lens, scores, s, note);
 }
 
 }  // namespace msa

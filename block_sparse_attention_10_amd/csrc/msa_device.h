@@ -47,6 +47,11 @@ __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t codes) {
                             __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, HI));
 }
 
+// Two OCP E4M3 codes (low 16 bits of `codes`) -> fp32 pair, exact.
+__device__ __forceinline__ f32x2 e4m3x2_to_f32x2(uint32_t codes) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(codes, 1.0f, false);
+}
+
 // One OCP E4M3 code (low byte of `code`) -> fp32.
 __device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
   f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(code & 0xFFu, 1.0f, false);
@@ -62,6 +67,14 @@ __device__ __forceinline__ f32x2 e2m1x2_to_f32x2(uint32_t packed, int sel) {
     case 2: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, 1.0f, 2);
     default: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, 1.0f, 3);
   }
+}
+
+// Byte SEL of `packed` holds two OCP E2M1 codes (element 2j in the low
+// nibble) -> the two values, unscaled, as a packed bf16 pair (exact).
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1x2_to_bf16x2(uint32_t packed) {
+  return __builtin_bit_cast(uint32_t,
+                            __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, 1.0f, SEL));
 }
 
 // Pack the upper halves of two fp32 values into a bf16 pair (truncation).

@@ -36,8 +36,9 @@ struct Workspace {
 Workspace workspace_layout(const Dims& d);
 
 hipError_t launch_index_scan(const Dims& d, const void* idx_q, const void* idx_k,
-                             const int32_t* block_table, const int32_t* ctx_lens,
-                             float* scores, hipStream_t s, std::string* note);
+                             const void* idx_k_scale, const int32_t* block_table,
+                             const int32_t* ctx_lens, float* scores, hipStream_t s,
+                             std::string* note);
 
 hipError_t launch_select(const Dims& d, const float* scores, const int32_t* ctx_lens,
                          const int32_t* block_table, int32_t* selected, int32_t* n_selected,

@@ -71,6 +71,12 @@ __global__ void fill_small_ints(void* p, size_t n, uint32_t salt) {
   }
 }
 
+__global__ void fill_hash_bytes(uint8_t* p, size_t n, uint32_t salt) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = (uint8_t)hash32((uint32_t)i ^ salt);
+}
+
 __global__ void fill_f32(float* p, size_t n, float v) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (size_t)gridDim.x * blockDim.x)
@@ -127,6 +133,7 @@ int main(int argc, char** argv) {
   }
   const size_t R = (size_t)B * T;
   const int kvc = dtype_code(kv), idc = dtype_code(idx);
+  // index-key bytes per element: bf16 2, fp8 1 (4-bit: half a byte, below)
   const size_t ie = idc == MSA_DTYPE_BF16 ? 2 : 1;
   const size_t rows = (size_t)NB * Hkv * 128;
   const size_t kv_row = kvc == MSA_DTYPE_BF16 ? 256 : (kvc == MSA_DTYPE_FP8_E4M3 ? 128 : 64);
@@ -151,11 +158,22 @@ int main(int argc, char** argv) {
   hipLaunchKernelGGL(fill_small_ints<2>, dim3(256), dim3(256), 0, 0, iq, R * Hidx * 64, 17u);
   t.idx_q = iq;
   const size_t ik_elems = (size_t)NB * Hidx * 128 * 64;
-  void* ik = dalloc(ik_elems * ie);
-  if (ie == 2)
-    hipLaunchKernelGGL(fill_small_ints<2>, dim3(4096), dim3(256), 0, 0, ik, ik_elems, 91u);
-  else
-    hipLaunchKernelGGL(fill_small_ints<1>, dim3(4096), dim3(256), 0, 0, ik, ik_elems, 91u);
+  void* ik;
+  if (idc == MSA_DTYPE_NVFP4) {
+    // random E2M1 code pairs, every scale 2.0
+    ik = dalloc(ik_elems / 2);
+    hipLaunchKernelGGL(fill_hash_bytes, dim3(4096), dim3(256), 0, 0, (uint8_t*)ik, ik_elems / 2,
+                       91u);
+    void* iks = dalloc(ik_elems / 16);
+    CHECK(hipMemset(iks, 0x40, ik_elems / 16));
+    t.idx_k_scale = iks;
+  } else {
+    ik = dalloc(ik_elems * ie);
+    if (ie == 2)
+      hipLaunchKernelGGL(fill_small_ints<2>, dim3(4096), dim3(256), 0, 0, ik, ik_elems, 91u);
+    else
+      hipLaunchKernelGGL(fill_small_ints<1>, dim3(4096), dim3(256), 0, 0, ik, ik_elems, 91u);
+  }
   t.idx_k_pool = ik;
   float* scores = (float*)dalloc(R * MAXB * 4);
 
@@ -214,7 +232,9 @@ int main(int argc, char** argv) {
   char rec[512];
   msa_last_dispatch(rec, sizeof(rec));
   size_t idx_bytes = 0;
-  for (int b = 0; b < B; ++b) idx_bytes += (size_t)((ctx[b] + 127) / 128) * Hidx * 128 * 64 * ie;
+  // per (token, index head): 64 elements, plus 4 scale codes for 4-bit keys
+  const size_t tok_bytes = idc == MSA_DTYPE_NVFP4 ? 32 + 4 : 64 * ie;
+  for (int b = 0; b < B; ++b) idx_bytes += (size_t)((ctx[b] + 127) / 128) * Hidx * 128 * tok_bytes;
   printf("%s launches %d index_key_bytes_per_launch %zu dispatch %s\n", mode.c_str(), launches,
          idx_bytes, rec);
   return 0;

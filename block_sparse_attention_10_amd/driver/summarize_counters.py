@@ -76,9 +76,9 @@ def read_spec(path):
 
 def index_key_bytes(spec):
     """Bytes of the index keys of every causal block: the scan's input."""
-    elem = 2 if spec["idx"] == "bf16" else 1
+    per_tok = {"bf16": 128, "fp8": 64, "nvfp4": 36}[spec["idx"]]  # bytes per token and head
     blocks = sum((L + 127) // 128 for L in spec["ctx"])
-    return blocks * spec["Hidx"] * 128 * 64 * elem
+    return blocks * spec["Hidx"] * 128 * per_tok
 
 
 def counter_table(paths):

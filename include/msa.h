@@ -37,7 +37,11 @@
  *  - Layouts (NB = num_phys_blocks, MAXB = max_blocks_per_seq, R = B * T):
  *      q           [R][Hq][head_dim]                bf16
  *      idx_q       [R][Hidx][idx_dim]               bf16
- *      idx_k_pool  [NB][Hidx][block_size][idx_dim]  bf16 or fp8 e4m3 codes
+ *      idx_k_pool  [NB][Hidx][block_size][idx_dim]  bf16 or fp8 e4m3 codes, or
+ *                  [NB][Hidx][block_size][idx_dim/2] bytes of two e2m1 codes
+ *                  (MSA_DTYPE_NVFP4, element 2j in the low nibble) with
+ *      idx_k_scale [NB][Hidx][block_size][idx_dim/16] e4m3 codes, one per 16
+ *                  consecutive elements (NULL for the other index dtypes)
  *      k_pool, v_pool
  *        MSA_DTYPE_BF16     [NB][Hkv][block_size][head_dim] bf16
  *        MSA_DTYPE_FP8_E4M3 [NB][Hkv][block_size][head_dim] e4m3 codes, and
@@ -106,7 +110,7 @@ typedef struct msa_problem {
   int32_t max_blocks_per_seq; /* MAXB: row length of block_table              */
   int32_t num_phys_blocks;    /* NB: blocks in each pool                      */
   int32_t kv_dtype;           /* MSA_DTYPE_BF16 / _FP8_E4M3 / _NVFP4          */
-  int32_t idx_k_dtype;        /* MSA_DTYPE_BF16 / _FP8_E4M3                   */
+  int32_t idx_k_dtype;        /* MSA_DTYPE_BF16 / _FP8_E4M3 / _NVFP4          */
   float sm_scale;             /* softmax scale; 0 means 1/sqrt(head_dim)      */
   uint32_t flags;             /* reserved, must be 0                          */
 } msa_problem;
@@ -121,13 +125,18 @@ typedef struct msa_tensors {
   const void* idx_k_pool;
   const int32_t* block_table;
   const int32_t* ctx_lens;
+  const void* idx_k_scale;    /* 4-bit index keys only, else NULL             */
 } msa_tensors;
 
 /* Step 1, block scoring (agentlenshq page, section "MSA 実行プロセス", step 1).
  * block_scores[r][c] = max over tokens i of logical block c with i <= p of
  * sum over index heads h and dims d of idx_q[r][h][d] * k_idx[i][h][d]
  * (no scale, no activation), accumulated in fp32; -inf for c > p / 128.
- * Reads t->idx_q, t->idx_k_pool, t->block_table, t->ctx_lens.  One launch. */
+ * 4-bit keys are e2m1 code x e4m3 scale; the dot product is summed per
+ * group of 16 dims and each group sum scaled (exact whenever products and
+ * partial sums fit fp32, as for integer queries and power-of-two scales).
+ * Reads t->idx_q, t->idx_k_pool, t->idx_k_scale (4-bit keys),
+ * t->block_table, t->ctx_lens.  One launch. */
 int msa_index_score(const msa_problem* p, const msa_tensors* t, float* block_scores,
                     void* stream);
 
@@ -192,11 +201,14 @@ int msa_last_hip_error(void);
 int msa_last_dispatch(char* buf, size_t n);
 
 /* Diagnostics: decode every OCP E4M3 and E2M1 code with the device decoders
- * the kernels use, into out[544] fp32 (device pointer, 16-byte aligned):
+ * the kernels use, into out[832] fp32 (device pointer, 16-byte aligned):
  *   out[c]            E4M3 code c (0..255) via the bf16 path (K/V, index keys)
- *   out[256 + c]      E2M1 code c (0..15) in the low nibble of a byte
- *   out[272 + c]      E2M1 code c (0..15) in the high nibble of a byte
- *   out[288 + c]      E4M3 code c (0..255) via the fp32 path (4-bit KV scales)
+ *   out[256 + c]      E2M1 code c (0..15) in the low nibble of a byte (fp32)
+ *   out[272 + c]      E2M1 code c (0..15) in the high nibble of a byte (fp32)
+ *   out[288 + c]      E4M3 code c (0..255) via the fp32 path (4-bit scales)
+ *   out[544 + c]      E2M1 code c in the low nibble, bf16 path (index keys)
+ *   out[560 + c]      E2M1 code c in the high nibble, bf16 path
+ *   out[576 + c]      E4M3 code c (0..255) as the second code of an fp32 pair
  * One launch. */
 int msa_selftest_decoders(float* out, void* stream);
 

@@ -202,8 +202,14 @@ CONFIGS: Dict[str, MSAConfig] = {
                                  kv_dtype="fp8", idx_dtype="fp8", n_plant=0, seed=1003),
     "ctx_1m_nvfp4": MSAConfig("ctx_1m_nvfp4", 4, 1, 64, 4, 4, 1048576, 1048576,
                               kv_dtype="nvfp4", idx_dtype="fp8", n_plant=16, seed=1004),
+    # the 128K layer with 4-bit index keys (E2M1 + E4M3 per 16 dims): the
+    # next index-cache format, 36 bytes per token and index head
+    "layer_128k_nvfp4_index": MSAConfig("layer_128k_nvfp4_index", 64, 1, 64, 4, 4, 8192, 131072,
+                                        idx_dtype="nvfp4", n_plant=8, seed=1005),
 }
 CONFIG_ORDER = ["tiny_4k", "tp8_rank_32k", "layer_128k", "spec_verify_fp8", "ctx_1m_nvfp4"]
+# workloads beyond the five above (formats the path supports next)
+EXTRA_CONFIGS = ["layer_128k_nvfp4_index"]
 
 
 @dataclass

@@ -30,7 +30,8 @@ def describe_workload(w: Workload):
     t = w.tensors
     return msa.describe(t["q"], t["idx_q"], t["k_pool"], t["v_pool"], t["k_scale"], t["v_scale"],
                         t["idx_k_pool"], t["block_table"], t["ctx_lens"],
-                        decode_query_len=w.cfg.query_len, topk=w.cfg.topk)
+                        decode_query_len=w.cfg.query_len, topk=w.cfg.topk,
+                        idx_k_scale=t.get("idx_k_scale"))
 
 
 def alloc_outputs(w: Workload, p):
@@ -101,14 +102,16 @@ def oracle_rows(w: Workload, rows):
         mini = problem_of(c)
         mini.batch = 1
         mini.max_blocks = nblk
+        iks = t.get("idx_k_scale")
         idx = {
             "idx_q": _host(t["idx_q"][b * T:(b + 1) * T]),
             "idx_k_pool": _host(t["idx_k_pool"][bt_row]),
+            "idx_k_scale": None if iks is None else _host(iks[bt_row]),
             "bt": np.arange(nblk, dtype=np.int32)[None, :],
             "ctx": np.array([L], dtype=np.int32),
         }
         s = oracle.index_scores(mini, idx["idx_q"], idx["idx_k_pool"], idx["bt"], idx["ctx"],
-                                local_rows)
+                                local_rows, idx_k_scale=idx["idx_k_scale"])
         sel, nsel = oracle.select(mini, s, idx["ctx"], local_rows)
         pt = oracle.page_table(mini, sel, _host(bt_all[b:b + 1, :nblk]), local_rows)
         # attention on a pool holding only the selected blocks

@@ -101,6 +101,15 @@ def test_null_and_misaligned_pointers_are_rejected():
     t2 = msa.Tensors(a, a + 8, a, a, None, None, a, a, a)
     assert L.msa_index_score(ctypes.byref(p), ctypes.byref(t2), ctypes.c_void_p(a),
                              None) == msa.MSA_ERR_INVALID_ARG
+    # 4-bit index keys need their (aligned) scale pool
+    p4 = good(idx_k_dtype="nvfp4")
+    assert L.msa_index_score(ctypes.byref(p4), ctypes.byref(t), ctypes.c_void_p(a),
+                             None) == msa.MSA_ERR_INVALID_ARG
+    t4 = msa.Tensors(a, a, a, a, None, None, a, a, a, a + 2)
+    assert L.msa_index_score(ctypes.byref(p4), ctypes.byref(t4), ctypes.c_void_p(a),
+                             None) == msa.MSA_ERR_INVALID_ARG
+    assert L.msa_decode(ctypes.byref(p4), ctypes.byref(t), None, None, ctypes.c_void_p(a),
+                        ctypes.c_void_p(a), 1 << 30, None) == msa.MSA_ERR_INVALID_ARG
     # fp8 KV needs its scales
     p8 = good(kv_dtype="fp8")
     assert L.msa_sparse_decode(ctypes.byref(p8), ctypes.byref(t), ctypes.c_void_p(a),

@@ -11,7 +11,7 @@ import torch
 
 import block_sparse_attention_10_amd as msa
 import oracle
-from synth import CONFIG_ORDER, CONFIGS, make_workload, small_config
+from synth import CONFIG_ORDER, CONFIGS, EXTRA_CONFIGS, make_workload, small_config
 from tests.msa_gpu import (TOL, check_invariants, compare_rows, oracle_attention_rows,
                            oracle_rows, problem_for, run_fused, run_stages, tensors_for)
 
@@ -25,19 +25,19 @@ def _say(msg):
 
 
 def test_device_decoders_match_oracle():
-    out = torch.empty(544, dtype=torch.float32, device=DEV)
+    out = torch.empty(832, dtype=torch.float32, device=DEV)
     msa.msa_selftest_decoders(out)
     torch.cuda.synchronize()
     o = out.cpu().numpy().astype(np.float64)
     e4 = np.array([oracle.e4m3_to_double(c) for c in range(256)])
     e2 = np.array([oracle.e2m1_to_double(c) for c in range(16)])
-    for base in (0, 288):
+    for base in (0, 288, 576):
         got = o[base:base + 256]
         nan = np.isnan(e4)
         assert np.array_equal(np.isnan(got), nan), f"NaN codes differ (base {base})"
         assert np.array_equal(got[~nan], e4[~nan]), f"e4m3 decode differs (base {base})"
-    assert np.array_equal(o[256:272], e2), "e2m1 low nibble"
-    assert np.array_equal(o[272:288], e2), "e2m1 high nibble"
+    for base in (256, 272, 544, 560):
+        assert np.array_equal(o[base:base + 16], e2), f"e2m1 decode differs (base {base})"
 
 
 SMALL = [
@@ -55,6 +55,13 @@ SMALL = [
     dict(batch=3, query_len=2, ctx_list=(2, 256, 1280), topk=1, seed=9),
     dict(batch=1, query_len=16, ctx_list=(4096,), num_q_heads=16, num_kv_heads=1,
          num_idx_heads=16, seed=10),
+    # 4-bit index keys, 1 / 2 / 4 rows per scan pass, ragged contexts
+    dict(batch=3, query_len=1, ctx_lo=1, ctx_hi=9000, idx_dtype="nvfp4", num_idx_heads=4,
+         n_plant=4, seed=23),
+    dict(batch=2, query_len=2, ctx_lo=2000, ctx_hi=12000, idx_dtype="nvfp4", num_idx_heads=2,
+         num_q_heads=16, num_kv_heads=2, seed=24),
+    dict(batch=2, query_len=5, ctx_lo=300, ctx_hi=6000, idx_dtype="nvfp4", kv_dtype="fp8",
+         seed=25),
 ]
 
 
@@ -190,10 +197,10 @@ def test_workspace_too_small_is_rejected():
 
 # --------------------------------------------------------- full workloads
 SAMPLE_ROWS = {"tiny_4k": None, "tp8_rank_32k": 6, "layer_128k": 6, "spec_verify_fp8": 12,
-               "ctx_1m_nvfp4": 4}
+               "ctx_1m_nvfp4": 4, "layer_128k_nvfp4_index": 6}
 
 
-@pytest.mark.parametrize("name", CONFIG_ORDER)
+@pytest.mark.parametrize("name", CONFIG_ORDER + EXTRA_CONFIGS)
 def test_full_workload_parity(name):
     cfg = CONFIGS[name]
     _say(f"full workload {name}: generating")
