@@ -26,7 +26,7 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
 METRIC = "MSA decode query-tokens/s at 128K ctx; achieved HBM GB/s vs peak"
 SCAN_KERNEL_SRCS = [os.path.join(ROOT, "block_sparse_attention_10_amd", "csrc", f)
                     for f in ("index_scan.hip", "msa_device.h")]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "msa_decode_layer_128k_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "msa_decode_{}_traffic.json")
 
 
 def kv_elem_bytes(kv):
@@ -74,12 +74,13 @@ def source_hash(paths):
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per scan launch from committed rocprofv3 counter runs, if
-    they were taken on the current scan kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
+def measured_traffic(workload):
+    """HBM bytes per scan launch from committed rocprofv3 counter runs on
+    this workload, if they were taken on the current scan kernel source."""
+    path = TRAFFIC_FILE.format(workload)
+    if not os.path.exists(path):
         return None
-    rec = json.load(open(TRAFFIC_FILE)).get("kernels", {}).get("index_scan", {})
+    rec = json.load(open(path)).get("kernels", {}).get("index_scan", {})
     if rec.get("kernel_source_sha256_16") != source_hash(SCAN_KERNEL_SRCS):
         return None
     return rec.get("hbm_bytes_per_launch")
@@ -298,7 +299,7 @@ def main():
             "frac": achieved / PEAK_HBM_GBS,
             "avg_launch_us": scan_us,
             "algorithmic_bytes_per_launch": ab["index"],
-            "traffic": measured_traffic() if cfg.name == "layer_128k" else None,
+            "traffic": measured_traffic(cfg.name),
         },
     }
     if not args.no_cpu_baseline:

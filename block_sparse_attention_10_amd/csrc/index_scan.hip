@@ -77,6 +77,80 @@ __device__ __forceinline__ void scan_block(const uint16_t* __restrict__ idx_q,
     sblk = idx_ks + phys * Hidx * (kBlock * 4) + (lane >> 1) * 4 + (lane & 1) * 2;
   const int dim0 = (lane % LPT) * DPL;
 
+  // one index head's loads: keys (and 4-bit scales) of the block, queries
+  struct Head {
+    u32x4 kv[NLD];
+    uint32_t ks[NLD];
+    uint32_t qv[TR][QW];
+  };
+  auto load_head = [&](Head& hd, int h, int t0) {
+    const uint8_t* kh = kblk + (size_t)h * head_bytes;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) hd.kv[i] = ldg128_stream(kh + i * 1024);
+    if constexpr (KIND == kFp4) {
+      const uint8_t* sh = sblk + (size_t)h * (kBlock * 4);
+#pragma unroll
+      for (int i = 0; i < NLD; ++i)
+        hd.ks[i] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(sh + i * 128));
+    }
+#pragma unroll
+    for (int t = 0; t < TR; ++t) {
+      const int row = b * T + min(t0 + t, T - 1);
+      const uint16_t* qp = idx_q + ((size_t)row * Hidx + h) * kIdxDim + dim0;
+#pragma unroll
+      for (int w = 0; w < QW; w += 4) {
+        u32x4 v = ldg128(qp + 2 * w);
+        hd.qv[t][w] = v.x; hd.qv[t][w + 1] = v.y; hd.qv[t][w + 2] = v.z; hd.qv[t][w + 3] = v.w;
+      }
+    }
+  };
+  auto score_head = [&](const Head& hd, float (&part)[TR][NLD]) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      uint32_t kw[QW];
+      const uint32_t src[4] = {hd.kv[i].x, hd.kv[i].y, hd.kv[i].z, hd.kv[i].w};
+      if constexpr (KIND == kBf16) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) kw[w] = src[w];
+      } else if constexpr (KIND == kFp8) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          kw[2 * w] = e4m3x2_to_bf16x2<false>(src[w]);
+          kw[2 * w + 1] = e4m3x2_to_bf16x2<true>(src[w]);
+        }
+      } else {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          kw[4 * w] = e2m1x2_to_bf16x2<0>(src[w]);
+          kw[4 * w + 1] = e2m1x2_to_bf16x2<1>(src[w]);
+          kw[4 * w + 2] = e2m1x2_to_bf16x2<2>(src[w]);
+          kw[4 * w + 3] = e2m1x2_to_bf16x2<3>(src[w]);
+        }
+      }
+      if constexpr (KIND == kFp4) {
+        // dims 0..15 of the lane under scale 0, 16..31 under scale 1
+        const f32x2 sc = e4m3x2_to_f32x2(hd.ks[i]);
+#pragma unroll
+        for (int t = 0; t < TR; ++t) {
+          float g0 = 0.f, g1 = 0.f;
+#pragma unroll
+          for (int w = 0; w < QW / 2; ++w) g0 = dot2_bf16(kw[w], hd.qv[t][w], g0);
+#pragma unroll
+          for (int w = QW / 2; w < QW; ++w) g1 = dot2_bf16(kw[w], hd.qv[t][w], g1);
+          part[t][i] = fmaf(sc.y, g1, fmaf(sc.x, g0, part[t][i]));
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < TR; ++t) {
+          float acc = part[t][i];
+#pragma unroll
+          for (int w = 0; w < QW; ++w) acc = dot2_bf16(kw[w], hd.qv[t][w], acc);
+          part[t][i] = acc;
+        }
+      }
+    }
+  };
+
   for (int t0 = 0; t0 < T; t0 += TR) {
     float part[TR][NLD];
 #pragma unroll
@@ -84,73 +158,12 @@ __device__ __forceinline__ void scan_block(const uint16_t* __restrict__ idx_q,
 #pragma unroll
       for (int i = 0; i < NLD; ++i) part[t][i] = 0.f;
 
+    // (keeping the next head's loads in flight was measured no faster for
+    // 4-bit keys: it costs occupancy that 16 waves per CU already cover)
     for (int h = 0; h < Hidx; ++h) {
-      u32x4 kv[NLD];
-      uint32_t ks[NLD];
-      const uint8_t* kh = kblk + (size_t)h * head_bytes;
-#pragma unroll
-      for (int i = 0; i < NLD; ++i) kv[i] = ldg128_stream(kh + i * 1024);
-      if constexpr (KIND == kFp4) {
-        const uint8_t* sh = sblk + (size_t)h * (kBlock * 4);
-#pragma unroll
-        for (int i = 0; i < NLD; ++i)
-          ks[i] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(sh + i * 128));
-      }
-      uint32_t qv[TR][QW];
-#pragma unroll
-      for (int t = 0; t < TR; ++t) {
-        const int row = b * T + min(t0 + t, T - 1);
-        const uint16_t* qp = idx_q + ((size_t)row * Hidx + h) * kIdxDim + dim0;
-#pragma unroll
-        for (int w = 0; w < QW; w += 4) {
-          u32x4 v = ldg128(qp + 2 * w);
-          qv[t][w] = v.x; qv[t][w + 1] = v.y; qv[t][w + 2] = v.z; qv[t][w + 3] = v.w;
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < NLD; ++i) {
-        uint32_t kw[QW];
-        const uint32_t src[4] = {kv[i].x, kv[i].y, kv[i].z, kv[i].w};
-        if constexpr (KIND == kBf16) {
-#pragma unroll
-          for (int w = 0; w < 4; ++w) kw[w] = src[w];
-        } else if constexpr (KIND == kFp8) {
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            kw[2 * w] = e4m3x2_to_bf16x2<false>(src[w]);
-            kw[2 * w + 1] = e4m3x2_to_bf16x2<true>(src[w]);
-          }
-        } else {
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            kw[4 * w] = e2m1x2_to_bf16x2<0>(src[w]);
-            kw[4 * w + 1] = e2m1x2_to_bf16x2<1>(src[w]);
-            kw[4 * w + 2] = e2m1x2_to_bf16x2<2>(src[w]);
-            kw[4 * w + 3] = e2m1x2_to_bf16x2<3>(src[w]);
-          }
-        }
-        if constexpr (KIND == kFp4) {
-          // dims 0..15 of the lane under scale 0, 16..31 under scale 1
-          const f32x2 sc = e4m3x2_to_f32x2(ks[i]);
-#pragma unroll
-          for (int t = 0; t < TR; ++t) {
-            float g0 = 0.f, g1 = 0.f;
-#pragma unroll
-            for (int w = 0; w < QW / 2; ++w) g0 = dot2_bf16(kw[w], qv[t][w], g0);
-#pragma unroll
-            for (int w = QW / 2; w < QW; ++w) g1 = dot2_bf16(kw[w], qv[t][w], g1);
-            part[t][i] = fmaf(sc.y, g1, fmaf(sc.x, g0, part[t][i]));
-          }
-        } else {
-#pragma unroll
-          for (int t = 0; t < TR; ++t) {
-            float acc = part[t][i];
-#pragma unroll
-            for (int w = 0; w < QW; ++w) acc = dot2_bf16(kw[w], qv[t][w], acc);
-            part[t][i] = acc;
-          }
-        }
-      }
+      Head hd;
+      load_head(hd, h, t0);
+      score_head(hd, part);
     }
 
 #pragma unroll
