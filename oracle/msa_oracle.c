@@ -357,6 +357,137 @@ int msa_oracle_attention(const oracle_problem* p, const uint16_t* q, const void*
   return 0;
 }
 
+/* ---- the write path: quantising new tokens into the pools ------------- */
+/* The step before the hot path (news.ainew.jp MI355X article, section 3:
+ * the fused projection writes the index cache; aisoku.org article, section
+ * "何が新しいか": KV stored as fp8 or NVFP4).  The pages give no recipe, so
+ * these follow the plainest reading, the one the synthetic inputs use:
+ *  - fp8 K / V: per (token, head) scale = amax / 448 (1 when amax is 0),
+ *    code = E4M3 round-to-nearest-even of x / scale clamped to +-448;
+ *  - 4-bit K / V / index keys: per 16 elements s = E4M3 RNE of amax / 6,
+ *    code = E2M1 RNE of x / s saturating at 6, all codes 0 when s is 0;
+ *  - fp8 index keys: the E4M3 RNE code of the value itself (no scale).
+ * Every step that decides a code runs in fp32 (IEEE single: division and
+ * round-to-nearest-even), the precision the GPU kernel decides it in. */
+
+/* fp32 -> OCP E4M3 code, round-to-nearest-even, magnitudes saturating at
+ * 448; the sign is kept (negative values that round to 0 give 0x80). */
+uint8_t msa_oracle_f32_to_e4m3(float x) {
+  uint8_t sign = signbit(x) ? 0x80 : 0x00;
+  float a = fabsf(x);
+  if (isnan(a)) return (uint8_t)(sign | 0x7F);
+  if (a >= 448.0f) return (uint8_t)(sign | 0x7E);
+  if (a < 0.015625f) {                       /* below 2^-6: steps of 2^-9 */
+    float m = nearbyintf(a * 512.0f);        /* 0..8; 8 is the first normal */
+    return (uint8_t)(sign | (uint8_t)m);
+  }
+  int e2;
+  float f = frexpf(a, &e2);                  /* a = f * 2^e2, f in [0.5, 1) */
+  int e = e2 - 1;                            /* a = (2f) * 2^e, 2f in [1, 2) */
+  float m = nearbyintf((2.0f * f - 1.0f) * 8.0f);  /* 3 mantissa bits */
+  if (m == 8.0f) { m = 0.0f; e += 1; }
+  int code = ((e + 7) << 3) | (int)m;
+  if (code > 0x7E) code = 0x7E;
+  return (uint8_t)(sign | code);
+}
+
+/* fp32 -> OCP E2M1 code: round-to-nearest-even onto {0, .5, 1, 1.5, 2, 3,
+ * 4, 6}, saturating at 6; the sign bit only on a nonzero magnitude. */
+uint8_t msa_oracle_f32_to_e2m1(float x) {
+  float a = fabsf(x);
+  int m;
+  if (!(a < 6.0f)) m = 7;                               /* 6 (and NaN)      */
+  else if (a < 2.0f) m = (int)nearbyintf(a * 2.0f);     /* 0 .. 2 by 0.5   */
+  else if (a < 4.0f) m = 2 + (int)nearbyintf(a);        /* 2, 3, 4 -> 4..6 */
+  else m = 4 + (int)nearbyintf(a * 0.5f);               /* 4, 6 -> 6, 7    */
+  return (uint8_t)((x < 0.0f && m > 0) ? (m | 8) : m);
+}
+
+/* fp8 one row of n values: codes and the row's fp32 scale. */
+static void quantize_fp8_row(const float* x, int n, uint8_t* codes, float* scale) {
+  float amax = 0.0f;
+  for (int i = 0; i < n; i++) amax = fmaxf(amax, fabsf(x[i]));
+  float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+  for (int i = 0; i < n; i++) {
+    float y = x[i] / s;
+    if (y > 448.0f) y = 448.0f;
+    if (y < -448.0f) y = -448.0f;
+    codes[i] = msa_oracle_f32_to_e4m3(y);
+  }
+  *scale = s;
+}
+
+/* 4-bit one row of n values (n a multiple of 16): packed codes (element 2j
+ * in the low nibble of byte j) and one E4M3 scale code per 16 elements. */
+static void quantize_fp4_row(const float* x, int n, uint8_t* packed, uint8_t* scales) {
+  for (int g = 0; g < n / 16; g++) {
+    const float* v = x + 16 * g;
+    float amax = 0.0f;
+    for (int i = 0; i < 16; i++) amax = fmaxf(amax, fabsf(v[i]));
+    uint8_t sc = msa_oracle_f32_to_e4m3(amax / 6.0f);
+    float s = (float)msa_oracle_e4m3_to_double(sc);
+    scales[g] = sc;
+    for (int i = 0; i < 16; i += 2) {
+      uint8_t lo = s > 0.0f ? msa_oracle_f32_to_e2m1(v[i] / s) : 0;
+      uint8_t hi = s > 0.0f ? msa_oracle_f32_to_e2m1(v[i + 1] / s) : 0;
+      packed[(16 * g + i) / 2] = (uint8_t)(lo | (hi << 4));
+    }
+  }
+}
+
+/* Writes the T new tokens of every request: row r = b T + t is the token at
+ * position p = ctx_lens[b] - T + t, stored at slot p mod 128 of physical
+ * block block_table[b][p / 128].  k_new, v_new [R][Hkv][head_dim] and
+ * idx_new [R][Hidx][idx_dim] are bf16 bit patterns; each row of each head is
+ * quantised to the pool's format.  Pools as the attention reads them. */
+int msa_oracle_insert(const oracle_problem* p, const uint16_t* k_new, const uint16_t* v_new,
+                      const uint16_t* idx_new, const int32_t* block_table,
+                      const int32_t* ctx_lens, void* k_pool, void* v_pool, void* k_scale,
+                      void* v_scale, void* idx_k_pool, void* idx_k_scale) {
+  int T = p->query_len, D = p->head_dim, E = p->idx_dim, BS = p->block_size;
+  int R = p->batch * T;
+  float buf[256];
+  for (int r = 0; r < R; r++) {
+    int b = r / T, t = r % T;
+    int64_t pos = row_position(ctx_lens[b], T, t);
+    int64_t phys = block_table[(int64_t)b * p->max_blocks + pos / BS];
+    int64_t slot = pos % BS;
+    for (int kv = 0; kv < 2; kv++) {
+      const uint16_t* src = kv ? v_new : k_new;
+      void* pool = kv ? v_pool : k_pool;
+      void* scale = kv ? v_scale : k_scale;
+      for (int g = 0; g < p->num_kv_heads; g++) {
+        const uint16_t* x = src + ((int64_t)r * p->num_kv_heads + g) * D;
+        int64_t row = (phys * p->num_kv_heads + g) * BS + slot;
+        for (int i = 0; i < D; i++) buf[i] = (float)msa_oracle_bf16_to_double(x[i]);
+        if (p->kv_dtype == ORACLE_BF16)
+          memcpy((uint16_t*)pool + row * D, x, (size_t)D * 2);
+        else if (p->kv_dtype == ORACLE_FP8)
+          quantize_fp8_row(buf, D, (uint8_t*)pool + row * D, (float*)scale + row);
+        else
+          quantize_fp4_row(buf, D, (uint8_t*)pool + row * (D / 2),
+                           (uint8_t*)scale + row * (D / 16));
+      }
+    }
+    for (int h = 0; h < p->num_idx_heads; h++) {
+      const uint16_t* x = idx_new + ((int64_t)r * p->num_idx_heads + h) * E;
+      int64_t row = (phys * p->num_idx_heads + h) * BS + slot;
+      for (int i = 0; i < E; i++) buf[i] = (float)msa_oracle_bf16_to_double(x[i]);
+      if (p->idx_dtype == ORACLE_BF16)
+        memcpy((uint16_t*)idx_k_pool + row * E, x, (size_t)E * 2);
+      else if (p->idx_dtype == ORACLE_FP8)
+        for (int i = 0; i < E; i++) {
+          float y = buf[i] > 448.0f ? 448.0f : (buf[i] < -448.0f ? -448.0f : buf[i]);
+          ((uint8_t*)idx_k_pool)[row * E + i] = msa_oracle_f32_to_e4m3(y);
+        }
+      else
+        quantize_fp4_row(buf, E, (uint8_t*)idx_k_pool + row * (E / 2),
+                         (uint8_t*)idx_k_scale + row * (E / 16));
+    }
+  }
+  return 0;
+}
+
 /* Number of worker threads the parallel loops above use. */
 int msa_oracle_num_threads(void) {
 #ifdef _OPENMP

@@ -102,6 +102,11 @@ def lib():
         L.msa_oracle_attention.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                            ctypes.c_int32, vp]
         L.msa_oracle_num_threads.restype = ctypes.c_int
+        L.msa_oracle_f32_to_e4m3.restype = ctypes.c_uint8
+        L.msa_oracle_f32_to_e4m3.argtypes = [ctypes.c_float]
+        L.msa_oracle_f32_to_e2m1.restype = ctypes.c_uint8
+        L.msa_oracle_f32_to_e2m1.argtypes = [ctypes.c_float]
+        L.msa_oracle_insert.argtypes = [pp] + [vp] * 11
         _lib = L
     return _lib
 
@@ -217,6 +222,37 @@ def decode(prob, q, idx_q, k_pool, v_pool, k_scale, v_scale, idx_k_pool, block_t
     pt = page_table(prob, sel, block_table, rows)
     out = attention(prob, q, k_pool, v_pool, k_scale, v_scale, block_table, ctx_lens, sel, rows)
     return {"scores": s, "selected": sel, "n_selected": nsel, "page_table": pt, "out": out}
+
+
+def f32_to_e4m3(x: float) -> int:
+    return int(lib().msa_oracle_f32_to_e4m3(x))
+
+
+def f32_to_e2m1(x: float) -> int:
+    return int(lib().msa_oracle_f32_to_e2m1(x))
+
+
+def insert(prob, k_new, v_new, idx_new, block_table, ctx_lens, pools):
+    """Write the T new tokens of every request into `pools` (a dict of host
+    arrays k_pool, v_pool, k_scale, v_scale, idx_k_pool, idx_k_scale in the
+    attention's layouts, modified in place), quantised to the pools'
+    formats.  k_new / v_new [R, Hkv, 128] and idx_new [R, Hidx, 64] are bf16
+    bit patterns (uint16)."""
+    for name in ("k_pool", "v_pool", "k_scale", "v_scale", "idx_k_pool", "idx_k_scale"):
+        a = pools.get(name)
+        if a is not None and not a.flags["C_CONTIGUOUS"]:
+            raise ValueError(f"{name} must be C-contiguous (it is written in place)")
+    k_new = _c(k_new, np.uint16)
+    v_new = _c(v_new, np.uint16)
+    idx_new = _c(idx_new, np.uint16)
+    block_table = _c(block_table, np.int32)
+    ctx_lens = _c(ctx_lens, np.int32)
+    p = prob.c()
+    lib().msa_oracle_insert(ctypes.byref(p), _ptr(k_new), _ptr(v_new), _ptr(idx_new),
+                            _ptr(block_table), _ptr(ctx_lens),
+                            *(_ptr(pools.get(n)) for n in ("k_pool", "v_pool", "k_scale",
+                                                           "v_scale", "idx_k_pool",
+                                                           "idx_k_scale")))
 
 
 def num_threads() -> int:

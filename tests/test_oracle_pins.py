@@ -437,3 +437,152 @@ def test_config_shapes_follow_page_heads():
         gold["heads_q_kv_idx"]["value"]
     assert [rank.num_q_heads, rank.num_kv_heads, rank.num_idx_heads] == \
         gold["tp8_rank_heads_q_kv_idx"]["value"]
+
+
+# -------------------------------------------------------------- write path
+def _f32(v):
+    return np.float32(v)
+
+
+def _e4m3_probe_values():
+    """Every E4M3 value, the midpoints between neighbours (exact ties), one
+    fp32 ulp either side of each midpoint, and random values over the whole
+    exponent range, both signs (magnitudes <= 448)."""
+    vals = decode_e4m3(np.arange(0x7F, dtype=np.uint8)).astype(np.float32)  # 0 .. 448
+    mids = ((vals[:-1].astype(np.float64) + vals[1:]) / 2).astype(np.float32)
+    up = np.nextafter(mids, np.float32(np.inf))
+    down = np.nextafter(mids, np.float32(-np.inf))
+    rng = np.random.default_rng(5)
+    rnd = (rng.standard_normal(4000) * np.exp2(rng.integers(-12, 8, 4000))).astype(np.float32)
+    rnd = np.clip(rnd, -448, 448)
+    pos = np.concatenate([vals, mids, up, down, np.abs(rnd), [1e-30, 2.0 ** -10]])
+    return np.concatenate([pos, -pos]).astype(np.float32)
+
+
+def test_e4m3_encoder_matches_torch_rounding():
+    x = _e4m3_probe_values()
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.f32_to_e4m3(float(v)) for v in x], dtype=np.uint8)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, [(float(x[i]), hex(got[i]), hex(want[i])) for i in bad[:5]]
+    assert oracle.f32_to_e4m3(1000.0) == 0x7E and oracle.f32_to_e4m3(-1000.0) == 0xFE
+
+
+def test_e2m1_encoder_is_nearest_even_on_the_grid():
+    grid = np.array(E2M1_TABLE[:8])
+    mids = (grid[:-1] + grid[1:]) / 2
+    pts = np.concatenate([grid, mids, np.nextafter(mids, 10), np.nextafter(mids, -10),
+                          np.linspace(0, 8, 801)]).astype(np.float32)
+    pts = np.concatenate([pts, -pts])
+    for v in pts:
+        a = abs(float(v))
+        d = np.abs(grid - min(a, 6.0))
+        best = np.flatnonzero(d == d.min())
+        m = int(best[0] if len(best) == 1 else best[best % 2 == 0][0])  # tie: even code
+        want = m | (8 if v < 0 and m > 0 else 0)
+        assert oracle.f32_to_e2m1(float(v)) == want, (float(v), want)
+    # and the generator's (independent, torch) encoder agrees
+    from synth import encode_e2m1
+    t = torch.from_numpy(pts)
+    assert np.array_equal(encode_e2m1(t).numpy(),
+                          np.array([oracle.f32_to_e2m1(float(v)) for v in pts], dtype=np.uint8))
+
+
+def _insert_case(kv_dtype, idx_dtype, seed=41, T=2):
+    cfg = small_config(batch=3, query_len=T, ctx_lo=200, ctx_hi=900, kv_dtype=kv_dtype,
+                       idx_dtype=idx_dtype, num_q_heads=8, num_kv_heads=2, num_idx_heads=2,
+                       seed=seed)
+    w = make_workload(cfg)
+    h = host_arrays(w)
+    rng = np.random.default_rng(seed)
+    R = cfg.rows
+    new = {
+        "k": torch.from_numpy(rng.standard_normal((R, 2, 128)).astype(np.float32) * 3),
+        "v": torch.from_numpy(rng.standard_normal((R, 2, 128)).astype(np.float32)),
+        "i": torch.from_numpy(rng.integers(-8, 9, (R, 2, 64)).astype(np.float32)),
+    }
+    bits = {k: v.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+            for k, v in new.items()}
+    pools = {k: (None if h[k] is None else h[k].copy())
+             for k in ("k_pool", "v_pool", "k_scale", "v_scale", "idx_k_pool", "idx_k_scale")}
+    oracle.insert(problem_of(cfg), bits["k"], bits["v"], bits["i"], h["block_table"],
+                  h["ctx_lens"], pools)
+    return cfg, w, h, new, pools
+
+
+def _slots(cfg, h):
+    T = cfg.query_len
+    for r in range(cfg.rows):
+        b, t = divmod(r, T)
+        p = int(h["ctx_lens"][b]) - T + t
+        yield r, int(h["block_table"][b, p // 128]), p % 128
+
+
+@pytest.mark.parametrize("kv,idx", [("bf16", "bf16"), ("fp8", "fp8"), ("nvfp4", "nvfp4")])
+def test_insert_writes_the_generators_encoding_at_each_rows_slot(kv, idx):
+    from synth import encode_fp8_per_token, encode_nvfp4
+    cfg, w, h, new, pools = _insert_case(kv, idx)
+    touched = {}
+    for r, phys, slot in _slots(cfg, h):
+        kf = new["k"][r].to(torch.bfloat16).float()
+        vf = new["v"][r].to(torch.bfloat16).float()
+        idf = new["i"][r].to(torch.bfloat16).float()
+        for name, x in (("k", kf), ("v", vf)):
+            got = pools[name + "_pool"][phys, :, slot]
+            if kv == "bf16":
+                assert np.array_equal(got, x.to(torch.bfloat16).view(torch.int16).numpy()
+                                      .view(np.uint16))
+            elif kv == "fp8":
+                c, s = encode_fp8_per_token(x)
+                assert np.array_equal(got, c.numpy())
+                assert np.array_equal(pools[name + "_scale"][phys, :, slot], s.numpy())
+            else:
+                c, s = encode_nvfp4(x)
+                assert np.array_equal(got, c.numpy())
+                assert np.array_equal(pools[name + "_scale"][phys, :, slot], s.numpy())
+        got = pools["idx_k_pool"][phys, :, slot]
+        if idx == "bf16":
+            assert np.array_equal(got, idf.to(torch.bfloat16).view(torch.int16).numpy()
+                                  .view(np.uint16))
+        elif idx == "fp8":
+            assert np.array_equal(got, idf.to(torch.float8_e4m3fn).view(torch.uint8).numpy())
+        else:
+            c, s = encode_nvfp4(idf)
+            assert np.array_equal(got, c.numpy())
+            assert np.array_equal(pools["idx_k_scale"][phys, :, slot], s.numpy())
+        touched.setdefault(phys, set()).add(slot)
+    # every other slot is untouched
+    for name in pools:
+        if pools[name] is None:
+            continue
+        a, b0 = pools[name], h[name]
+        for phys in range(a.shape[0]):
+            for slot in range(128):
+                if slot in touched.get(phys, ()):
+                    continue
+                assert np.array_equal(a[phys, :, slot], b0[phys, :, slot]), (name, phys, slot)
+
+
+def test_decode_after_insert_attends_the_new_token():
+    """A new key along the row's own query (scaled up) takes all the softmax
+    weight of the row: the output becomes the new value, dequantised."""
+    cfg = small_config(batch=2, query_len=1, ctx_lo=300, ctx_hi=800, num_q_heads=2,
+                       num_kv_heads=1, num_idx_heads=1, seed=43)
+    w = make_workload(cfg)
+    h = host_arrays(w)
+    q = decode_bf16(h["q"])                                  # [R, 2, 128]
+    k_new = torch.from_numpy((q.sum(axis=1, keepdims=True) * 64).astype(np.float32))
+    v_new = torch.from_numpy(np.random.default_rng(3).standard_normal((2, 1, 128))
+                             .astype(np.float32))
+    i_new = torch.zeros((2, 1, 64))
+    bits = [x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+            for x in (k_new, v_new, i_new)]
+    pools = {k: (None if h[k] is None else h[k].copy())
+             for k in ("k_pool", "v_pool", "k_scale", "v_scale", "idx_k_pool", "idx_k_scale")}
+    oracle.insert(problem_of(cfg), *bits, h["block_table"], h["ctx_lens"], pools)
+    h2 = dict(h, **pools)
+    res = run_oracle(cfg, h2)
+    want = v_new.to(torch.bfloat16).double().numpy()[:, 0]   # [R, 128]
+    for r in range(2):
+        for hq in range(2):
+            assert np.max(np.abs(res["out"][r, hq] - want[r])) < 1e-6
