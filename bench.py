@@ -258,6 +258,24 @@ def main():
     torch.cuda.synchronize()
     reuse_us = start.elapsed_time(end) / args.steps * 1e3
 
+    # the write path of a step: the R new tokens' K, V and index keys go into
+    # the pools (quantised to their formats); timed last, as it changes them
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    new = [torch.randn((R, H, Dh), generator=gen, device="cuda").to(torch.bfloat16)
+           for H, Dh in ((cfg.num_kv_heads, 128), (cfg.num_kv_heads, 128),
+                         (cfg.num_idx_heads, 64))]
+    pl = msa.pools(wt["k_pool"], wt["v_pool"], wt["k_scale"], wt["v_scale"], wt["idx_k_pool"],
+                   wt.get("idx_k_scale"))
+    for _ in range(args.warmup):
+        msa.msa_insert_kv(p, pl, wt["block_table"], wt["ctx_lens"], *new)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        msa.msa_insert_kv(p, pl, wt["block_table"], wt["ctx_lens"], *new)
+    end.record()
+    torch.cuda.synchronize()
+    insert_us = start.elapsed_time(end) / args.steps * 1e3
+
     rec = {
         "metric": METRIC,
         "value": cfg.rows / (ms * 1e-3),
@@ -284,6 +302,11 @@ def main():
             "achieved_GBps_end_to_end": ab["total"] / (ms * 1e-3) / 1e9,
             "frac_of_peak_end_to_end": ab["total"] / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
             "kernels": dispatch,
+            "insert": {
+                "us": insert_us,
+                "rows": R,
+                "note": "write path: K, V and index key of each row's new token into the pools",
+            },
             "reuse_layer": {
                 "us_per_layer": reuse_us,
                 "query_tokens_per_s": R / (reuse_us * 1e-6),

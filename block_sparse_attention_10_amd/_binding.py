@@ -26,7 +26,7 @@ DTYPES = {"bf16": 0, "fp8": 1, "nvfp4": 2}
 # Every symbol include/msa.h declares.
 EXPORTS = ("msa_index_score", "msa_select_blocks", "msa_build_page_table", "msa_sparse_decode",
            "msa_decode", "msa_workspace_bytes", "msa_status_string", "msa_last_hip_error",
-           "msa_last_dispatch", "msa_selftest_decoders")
+           "msa_last_dispatch", "msa_selftest_decoders", "msa_insert_kv")
 
 
 class MSAError(RuntimeError):
@@ -61,6 +61,11 @@ class Problem(ctypes.Structure):
     ]
 
 
+class Pools(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("k_pool", "v_pool", "k_scale", "v_scale", "idx_k_pool", "idx_k_scale")]
+
+
 class Tensors(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("q", "idx_q", "k_pool", "v_pool", "k_scale", "v_scale", "idx_k_pool",
@@ -80,7 +85,8 @@ def _load():
             ("msa_build_page_table", [pp, vp, vp, vp, vp]),
             ("msa_sparse_decode", [pp, tp, vp, vp, vp, sz, vp]),
             ("msa_decode", [pp, tp, vp, vp, vp, vp, sz, vp]),
-            ("msa_selftest_decoders", [vp, vp])):
+            ("msa_selftest_decoders", [vp, vp]),
+            ("msa_insert_kv", [pp, ctypes.POINTER(Pools), vp, vp, vp, vp, vp, vp])):
         f = getattr(L, name)
         f.argtypes = args
         f.restype = ctypes.c_int
@@ -162,6 +168,18 @@ def _stream(stream):
 def _check(status: int, fn: str):
     if status != MSA_OK:
         raise MSAError(status, fn)
+
+
+def pools(k_pool, v_pool, k_scale, v_scale, idx_k_pool, idx_k_scale=None) -> Pools:
+    return Pools(*(None if t is None else t.data_ptr() for t in
+                   (k_pool, v_pool, k_scale, v_scale, idx_k_pool, idx_k_scale)))
+
+
+def msa_insert_kv(p: Problem, pl: Pools, block_table, ctx_lens, k_new, v_new, idx_k_new,
+                  stream=None):
+    _check(_lib.msa_insert_kv(ctypes.byref(p), ctypes.byref(pl), _p(block_table), _p(ctx_lens),
+                              _p(k_new), _p(v_new), _p(idx_k_new), _stream(stream)),
+           "msa_insert_kv")
 
 
 def msa_index_score(p: Problem, t: Tensors, block_scores, stream=None):

@@ -223,6 +223,31 @@ int msa_decode(const msa_problem* p, const msa_tensors* t, int32_t* selected,
   return MSA_OK;
 }
 
+int msa_insert_kv(const msa_problem* p, const msa_pools* pools, const int32_t* block_table,
+                  const int32_t* ctx_lens, const void* k_new, const void* v_new,
+                  const void* idx_k_new, void* stream) {
+  Dims d;
+  int e;
+  if ((e = check_problem(p, &d))) return e;
+  if (!pools) return MSA_ERR_INVALID_ARG;
+  if ((e = check_ptr(pools->k_pool)) || (e = check_ptr(pools->v_pool)) ||
+      (e = check_ptr(pools->idx_k_pool)) || (e = check_ptr(block_table)) ||
+      (e = check_ptr(ctx_lens)) || (e = check_ptr(k_new)) || (e = check_ptr(v_new)) ||
+      (e = check_ptr(idx_k_new)))
+    return e;
+  if (d.kv_dtype != MSA_DTYPE_BF16 &&
+      ((e = check_ptr(pools->k_scale)) || (e = check_ptr(pools->v_scale))))
+    return e;
+  if (d.idx_dtype == MSA_DTYPE_NVFP4 && (e = check_ptr(pools->idx_k_scale))) return e;
+  const InsertPools pl = {pools->k_pool, pools->v_pool, pools->k_scale, pools->v_scale,
+                          pools->idx_k_pool, pools->idx_k_scale};
+  std::string note;
+  e = hip_status(launch_insert(d, k_new, v_new, idx_k_new, block_table, ctx_lens, pl,
+                               (hipStream_t)stream, &note));
+  if (e == MSA_OK) g_last_dispatch = note;
+  return e;
+}
+
 const char* msa_status_string(int status) {
   switch (status) {
     case MSA_OK: return "ok";

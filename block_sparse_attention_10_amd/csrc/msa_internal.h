@@ -55,6 +55,21 @@ hipError_t launch_sparse_attention(const Dims& d, const void* q, const void* k_p
                                    const int32_t* ctx_lens, float* part_o, float* part_ml,
                                    float* out, hipStream_t s, std::string* note);
 
+// Pools the write path fills (layouts as the attention reads them).
+struct InsertPools {
+  void* k_pool;
+  void* v_pool;
+  void* k_scale;
+  void* v_scale;
+  void* idx_k_pool;
+  void* idx_k_scale;
+};
+
+hipError_t launch_insert(const Dims& d, const void* k_new, const void* v_new,
+                         const void* idx_new, const int32_t* block_table,
+                         const int32_t* ctx_lens, const InsertPools& pools, hipStream_t s,
+                         std::string* note);
+
 hipError_t launch_selftest_decoders(float* out, hipStream_t s);
 
 }  // namespace msa

@@ -175,6 +175,38 @@ int msa_build_page_table(const msa_problem* p, const int32_t* selected,
 int msa_sparse_decode(const msa_problem* p, const msa_tensors* t, const int32_t* page_table,
                       float* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Pools the write path fills: the same buffers and layouts as in
+ * msa_tensors, writable.  Scale pools are NULL for bf16 data. */
+typedef struct msa_pools {
+  void* k_pool;
+  void* v_pool;
+  void* k_scale;
+  void* v_scale;
+  void* idx_k_pool;
+  void* idx_k_scale;
+} msa_pools;
+
+/* The write path that fills the pools this path reads (news.ainew.jp
+ * article, section 3: the fused projection writes each new token's index
+ * key into the index cache; aisoku.org article, section "何が新しいか": KV
+ * kept as fp8 / NVFP4).  Row r = b * T + t is the token at position
+ * p = ctx_lens[b] - T + t (ctx_lens already counts it); its K and V
+ * (k_new, v_new [R][Hkv][head_dim] bf16) and index key (idx_k_new
+ * [R][Hidx][idx_dim] bf16) are written to slot p mod 128 of physical block
+ * block_table[b][p / 128], quantised to the pools' dtypes:
+ *   fp8 K / V      scale = amax / 448 per (token, head) (1 if amax is 0),
+ *                  codes = E4M3 round-to-nearest-even of x / scale;
+ *   4-bit K / V / index keys
+ *                  per 16 elements scale code = E4M3(amax / 6), codes =
+ *                  E2M1 round-to-nearest-even of x / scale (saturating at
+ *                  6), all 0 when the scale is 0, negative zero as +0;
+ *   fp8 index keys E4M3 code of the value (no scale).
+ * Decisions are taken in fp32.  Rows must target distinct slots (a request's
+ * T rows do).  Nothing else in the pools changes.  One launch. */
+int msa_insert_kv(const msa_problem* p, const msa_pools* pools, const int32_t* block_table,
+                  const int32_t* ctx_lens, const void* k_new, const void* v_new,
+                  const void* idx_k_new, void* stream);
+
 /* Steps 1-4 in one call: the index scan, the selection with the page table
  * built in the same launch, then the attention (and its merge launch when
  * rows are split).  selected / page_table may be NULL; when given they

@@ -143,3 +143,25 @@ def test_status_strings():
     for c in (-1, -2, -3, -4):
         assert msa.msa_status_string(c) != "unknown status"
     assert msa.msa_status_string(7) == "unknown status"
+
+
+def test_insert_arguments_are_checked_before_launch():
+    L = msa.lib()
+    a = 0x10000
+    pl = msa.Pools(a, a, None, None, a, None)
+    vp = ctypes.c_void_p
+    ok = (vp(a), vp(a), vp(a), vp(a), vp(a))
+    # no pools / a NULL new-row pointer / misaligned pointer
+    assert L.msa_insert_kv(ctypes.byref(good()), None, *ok, None) == msa.MSA_ERR_INVALID_ARG
+    assert L.msa_insert_kv(ctypes.byref(good()), ctypes.byref(pl), vp(a), vp(a), None, vp(a),
+                           vp(a), None) == msa.MSA_ERR_INVALID_ARG
+    assert L.msa_insert_kv(ctypes.byref(good()), ctypes.byref(pl), vp(a), vp(a + 4), vp(a),
+                           vp(a), vp(a), None) == msa.MSA_ERR_INVALID_ARG
+    # quantised pools need their scales
+    assert L.msa_insert_kv(ctypes.byref(good(kv_dtype="fp8")), ctypes.byref(pl), *ok,
+                           None) == msa.MSA_ERR_INVALID_ARG
+    assert L.msa_insert_kv(ctypes.byref(good(idx_k_dtype="nvfp4")), ctypes.byref(pl), *ok,
+                           None) == msa.MSA_ERR_INVALID_ARG
+    # an unsupported shape is reported as such
+    assert L.msa_insert_kv(ctypes.byref(good(head_dim=64)), ctypes.byref(pl), *ok,
+                           None) == msa.MSA_ERR_UNSUPPORTED
