@@ -162,7 +162,19 @@ def cpu_baseline(w, n_requests, min_seconds=10.0):
     return {"value": rows * passes / elapsed, "unit": "query-tokens/s",
             "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"{len(reqs)} of {c.batch} requests ({rows} query rows, full contexts), "
-                      f"{passes} passes, {elapsed:.1f} s"}
+                      f"{passes} passes, {elapsed:.1f} s",
+            "cpu": cpu_model(), "host_cpus": os.cpu_count()}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def main():
@@ -230,6 +242,22 @@ def main():
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
     dispatch = msa.msa_last_dispatch()
+
+    # cold-cache steps: each timed alone after a 1 GiB write that evicts the
+    # L2s and the 256 MB last-level cache (the flush is outside the events)
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    cold = []
+    for _ in range(min(args.steps, 20)):
+        flush.fill_(1.0)
+        start.record()
+        step()
+        end.record()
+        torch.cuda.synchronize()
+        cold.append(start.elapsed_time(end) * 1e3)
+    del flush
+    cold.sort()
+    cold_us = {"p10": cold[len(cold) // 10], "p50": cold[len(cold) // 2],
+               "p90": cold[(9 * len(cold)) // 10], "steps": len(cold)}
 
     # the dominant kernel alone: index-key scan, same stream, same buffers
     for _ in range(args.warmup):
@@ -302,6 +330,7 @@ def main():
             "achieved_GBps_end_to_end": ab["total"] / (ms * 1e-3) / 1e9,
             "frac_of_peak_end_to_end": ab["total"] / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
             "kernels": dispatch,
+            "step_us_after_cache_flush": cold_us,
             "insert": {
                 "us": insert_us,
                 "rows": R,
