@@ -41,21 +41,21 @@ __device__ __forceinline__ void fold_stage(float* v, int lane) {
   for (int j = 0; j < HALF; ++j) {
     const float send = up ? v[j] : v[j + HALF];
     const float keep = up ? v[j + HALF] : v[j];
-    v[j] = keep + __shfl_xor(send, MASK);
+    v[j] = keep + dpp_xor<MASK>(send);
   }
 }
 
 // Key formats of the index cache.
 enum KeyKind { kBf16 = 0, kFp8 = 1, kFp4 = 2 };
 
-// Scores of logical block c (a real block: c * 128 < L) for every row of
-// request b, written by lane 0.  TR: rows scored per pass (1, 2 or 4); more
-// rows loop.  idx_ks: the 4-bit keys' scale pool (unused otherwise).
+// Scores of logical block c (a real block: c * 128 < L, stored in physical
+// block phys_block) for every row of request b, written by lane 0.  TR: rows
+// scored per pass (1, 2 or 4); more rows loop.  idx_ks: the 4-bit keys'
+// scale pool (unused otherwise).
 template <int KIND, int TR>
 __device__ __forceinline__ void scan_block(const uint16_t* __restrict__ idx_q,
                                            const uint8_t* __restrict__ idx_k,
-                                           const uint8_t* __restrict__ idx_ks,
-                                           const int32_t* __restrict__ block_table,
+                                           const uint8_t* __restrict__ idx_ks, int phys_block,
                                            float* __restrict__ scores, int b, int c, int L, int T,
                                            int Hidx, int MAXB, int lane) {
   constexpr int DPL = KIND == kBf16 ? 8 : (KIND == kFp8 ? 16 : 32);  // dims per lane per load
@@ -68,7 +68,7 @@ __device__ __forceinline__ void scan_block(const uint16_t* __restrict__ idx_q,
   float* srow = scores + (size_t)b * T * MAXB + c;
   // bytes of one (block, head): LPT lane slices of 16 B per token
   const size_t head_bytes = (size_t)kBlock * LPT * 16;
-  const size_t phys = (size_t)block_table[(size_t)b * MAXB + c];
+  const size_t phys = (size_t)phys_block;
   const uint8_t* kblk = idx_k + phys * Hidx * head_bytes + lane * 16;
   // 4-bit scales [block][head][token][4]: this lane's two codes (its 32
   // dims) of token 32 i + lane / 2 sit at sblk + i * 128
@@ -207,13 +207,31 @@ __global__ __launch_bounds__(256) void index_scan_kernel(
   if (item >= B * MAXB) return;
   const int b = item / MAXB;
   const int c = item - b * MAXB;
+  // the table entry is in bounds for every c < MAXB: read it together with
+  // the context length instead of after it
+  int phys = block_table[(size_t)b * MAXB + c];
   const int L = ctx_lens[b];
+  asm volatile("" : "+s"(phys));  // keeps the table load ahead of the branch
   if (c * kBlock > L - 1) {
     float* srow = scores + (size_t)b * T * MAXB + c;
     for (int t = lane; t < T; t += kWave) srow[(size_t)t * MAXB] = -INFINITY;
     return;
   }
-  scan_block<KIND, TR>(idx_q, idx_k, idx_ks, block_table, scores, b, c, L, T, Hidx, MAXB, lane);
+  scan_block<KIND, TR>(idx_q, idx_k, idx_ks, phys, scores, b, c, L, T, Hidx, MAXB, lane);
+}
+
+// Workgroups per CU that a scan launch lets run at once.  The kernel uses
+// no LDS, so a dynamic LDS request of a share of the CU's 160 KiB caps
+// residency.  Measured on MI355X: with bf16 or fp8 keys the stream runs
+// faster with fewer waves in flight than the register limit allows -- 3
+// workgroups per CU on grids of 8192 workgroups or more (1.5-3% on the 128K
+// and 1M-context layers), 4 on smaller grids, where 3 leaves a short last
+// round; 4-bit keys spend more ALU work per byte and run best uncapped.
+constexpr size_t kLdsPerCu = 160 * 1024;
+
+size_t scan_lds_bytes(int kind, unsigned workgroups) {
+  if (kind == kFp4) return 0;
+  return kLdsPerCu / (workgroups >= 8192 ? 3 : 4);
 }
 
 template <int KIND>
@@ -226,19 +244,20 @@ hipError_t launch_kind(const Dims& d, const void* idx_q, const void* idx_k, cons
   const auto* k = static_cast<const uint8_t*>(idx_k);
   const auto* ks = static_cast<const uint8_t*>(idx_ks);
   const int tr = d.T == 1 ? 1 : (d.T == 2 ? 2 : 4);
+  const size_t lds = scan_lds_bytes(KIND, grid.x);
   if (tr == 1)
-    hipLaunchKernelGGL((index_scan_kernel<KIND, 1>), grid, block, 0, s, q, k, ks, bt, cl, scores,
+    hipLaunchKernelGGL((index_scan_kernel<KIND, 1>), grid, block, lds, s, q, k, ks, bt, cl, scores,
                        d.B, d.T, d.Hidx, d.MAXB);
   else if (tr == 2)
-    hipLaunchKernelGGL((index_scan_kernel<KIND, 2>), grid, block, 0, s, q, k, ks, bt, cl, scores,
+    hipLaunchKernelGGL((index_scan_kernel<KIND, 2>), grid, block, lds, s, q, k, ks, bt, cl, scores,
                        d.B, d.T, d.Hidx, d.MAXB);
   else
-    hipLaunchKernelGGL((index_scan_kernel<KIND, 4>), grid, block, 0, s, q, k, ks, bt, cl, scores,
+    hipLaunchKernelGGL((index_scan_kernel<KIND, 4>), grid, block, lds, s, q, k, ks, bt, cl, scores,
                        d.B, d.T, d.Hidx, d.MAXB);
   static const char* names[3] = {"bf16", "fp8", "nvfp4"};
   if (note)
     *note += std::string("index_scan<") + names[KIND] + ",rows" + std::to_string(tr) +
-             ">[grid=" + std::to_string(grid.x) + "x256]";
+             ">[grid=" + std::to_string(grid.x) + "x256,lds=" + std::to_string(lds) + "]";
   return hipGetLastError();
 }
 

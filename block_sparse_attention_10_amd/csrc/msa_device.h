@@ -96,10 +96,43 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
   return __builtin_bit_cast(float, b << 16);
 }
 
+// `v` from lane l ^ MASK of the same wave, for MASK 1, 2 or 4, by DPP lane
+// moves (no LDS round trip): quad permutes for 1 and 2; for 4 the lanes
+// without bit 2 take row_shl:4, the others row_shr:4.
+template <int MASK>
+__device__ __forceinline__ float dpp_xor(float v) {
+  const int x = __builtin_bit_cast(int, v);
+  if constexpr (MASK == 1) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true));
+  } else if constexpr (MASK == 2) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true));
+  } else {
+    static_assert(MASK == 4, "DPP xor for lane masks 1, 2 and 4");
+    const int up = __builtin_amdgcn_mov_dpp(x, 0x104, 0xF, 0xF, true);    // lane + 4
+    const int down = __builtin_amdgcn_mov_dpp(x, 0x114, 0xF, 0xF, true);  // lane - 4
+    return __builtin_bit_cast(float, (lane_id() & 4) ? down : up);
+  }
+}
+
+// One DPP step of a wave max; lanes outside `ROW_MASK` keep their value.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_max_step(float v) {
+  const int x = __builtin_bit_cast(int, v);
+  return fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(x, x, CTRL, ROW_MASK,
+                                                                        0xF, false)));
+}
+
+// Wave-wide max, returned to every lane: DPP within rows of 16 (quad swaps,
+// half-row and row mirrors), row broadcasts across rows, then lane 63.
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
-  return v;
+  v = dpp_max_step<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  v = dpp_max_step<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  v = dpp_max_step<0x141, 0xF>(v);  // row_half_mirror
+  v = dpp_max_step<0x140, 0xF>(v);  // row_mirror
+  v = dpp_max_step<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v = dpp_max_step<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
 }  // namespace msa
