@@ -33,16 +33,24 @@ constexpr int kIdxDim = 64;  // index head dimension
 
 // One butterfly stage of the transpose-reduce: lanes with `MASK` set keep
 // the upper half of their partials, the others the lower half, and each adds
-// its partner's copy of the half it keeps.
-template <int HALF, int MASK>
+// its partner's copy of the half it keeps.  DPP: partner values by DPP lane
+// moves, else by LDS-pipe shuffles.
+template <int HALF, int MASK, bool DPP>
 __device__ __forceinline__ void fold_stage(float* v, int lane) {
   const bool up = (lane & MASK) != 0;
 #pragma unroll
   for (int j = 0; j < HALF; ++j) {
     const float send = up ? v[j] : v[j + HALF];
     const float keep = up ? v[j + HALF] : v[j];
-    v[j] = keep + dpp_xor<MASK>(send);
+    v[j] = keep + (DPP ? dpp_xor<MASK>(send) : __shfl_xor(send, MASK));
   }
+}
+
+// Wave-wide max by LDS-pipe shuffles (the DPP form is wave_max).
+__device__ __forceinline__ float wave_max_shfl(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
+  return v;
 }
 
 // Key formats of the index cache.
@@ -59,6 +67,10 @@ __device__ __forceinline__ void scan_block(const uint16_t* __restrict__ idx_q,
                                            float* __restrict__ scores, int b, int c, int L, int T,
                                            int Hidx, int MAXB, int lane) {
   constexpr int DPL = KIND == kBf16 ? 8 : (KIND == kFp8 ? 16 : 32);  // dims per lane per load
+  // Cross-lane steps: DPP for bf16 and fp8 keys; the 4-bit scan, which does
+  // more VALU work per byte, measured about 10% slower with them (the
+  // compiler keeps fewer key loads in flight) and uses shuffles.
+  constexpr bool kDpp = KIND != kFp4;
   constexpr int LPT = kIdxDim / DPL; // lanes per token (8 / 4 / 2)
   constexpr int TPL = kWave / LPT;   // tokens per load instruction (8 / 16 / 32)
   constexpr int NLD = kBlock / TPL;  // loads per (block, head) (16 / 8 / 4)
@@ -171,14 +183,14 @@ __device__ __forceinline__ void scan_block(const uint16_t* __restrict__ idx_q,
       if (t0 + t >= T) break;
       float* v = part[t];
       if constexpr (LPT == 8) {
-        fold_stage<8, 4>(v, lane);
-        fold_stage<4, 2>(v, lane);
-        fold_stage<2, 1>(v, lane);
+        fold_stage<8, 4, kDpp>(v, lane);
+        fold_stage<4, 2, kDpp>(v, lane);
+        fold_stage<2, 1, kDpp>(v, lane);
       } else if constexpr (LPT == 4) {
-        fold_stage<4, 2>(v, lane);
-        fold_stage<2, 1>(v, lane);
+        fold_stage<4, 2, kDpp>(v, lane);
+        fold_stage<2, 1, kDpp>(v, lane);
       } else {
-        fold_stage<2, 1>(v, lane);
+        fold_stage<2, 1, kDpp>(v, lane);
       }
       // lane now holds the full scores of loads i = 2 * (lane % LPT) + e
       const int pos = L - T + t0 + t;
@@ -188,7 +200,7 @@ __device__ __forceinline__ void scan_block(const uint16_t* __restrict__ idx_q,
         const int tok = (2 * (lane % LPT) + e) * TPL + lane / LPT;
         if (c * kBlock + tok <= pos) best = fmaxf(best, v[e]);
       }
-      best = wave_max(best);
+      best = kDpp ? wave_max(best) : wave_max_shfl(best);
       if (lane == 0) srow[(size_t)(t0 + t) * MAXB] = best;
     }
   }
