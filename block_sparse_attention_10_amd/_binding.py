@@ -20,13 +20,17 @@ MSA_ERR_INVALID_ARG = -1
 MSA_ERR_UNSUPPORTED = -2
 MSA_ERR_WORKSPACE = -3
 MSA_ERR_HIP = -4
+MSA_ERR_BAD_DATA = -5
+
+MSA_FLAG_DEBUG_CHECKS = 1
 
 DTYPES = {"bf16": 0, "fp8": 1, "nvfp4": 2}
 
 # Every symbol include/msa.h declares.
 EXPORTS = ("msa_index_score", "msa_select_blocks", "msa_build_page_table", "msa_sparse_decode",
            "msa_decode", "msa_workspace_bytes", "msa_status_string", "msa_last_hip_error",
-           "msa_last_dispatch", "msa_selftest_decoders", "msa_insert_kv")
+           "msa_last_dispatch", "msa_selftest_decoders", "msa_insert_kv",
+           "msa_last_check_failure")
 
 
 class MSAError(RuntimeError):
@@ -35,6 +39,8 @@ class MSAError(RuntimeError):
         msg = _lib.msa_status_string(status).decode()
         if status == MSA_ERR_HIP:
             msg += f" (hip error {_lib.msa_last_hip_error()})"
+        if status == MSA_ERR_BAD_DATA:
+            msg += f" ({msa_last_check_failure()})"
         super().__init__(f"{fn}: {msg} [{status}]")
 
 
@@ -98,6 +104,8 @@ def _load():
     L.msa_last_hip_error.restype = ctypes.c_int
     L.msa_last_dispatch.argtypes = [ctypes.c_char_p, sz]
     L.msa_last_dispatch.restype = ctypes.c_int
+    L.msa_last_check_failure.argtypes = [ctypes.c_char_p, sz]
+    L.msa_last_check_failure.restype = ctypes.c_int
     return L
 
 
@@ -134,7 +142,7 @@ def tensors(q=None, idx_q=None, k_pool=None, v_pool=None, k_scale=None, v_scale=
 
 
 def describe(q, idx_q, k_pool, v_pool, k_scale, v_scale, idx_k_pool, block_table, ctx_lens,
-             decode_query_len=1, topk=16, sm_scale=0.0, idx_k_scale=None):
+             decode_query_len=1, topk=16, sm_scale=0.0, idx_k_scale=None, flags=0):
     """(Problem, Tensors) for device tensors in the boundary's layouts; the
     dimensions and dtypes are read from the tensor shapes (index keys with an
     idx_k_scale pool are 4-bit)."""
@@ -151,7 +159,7 @@ def describe(q, idx_q, k_pool, v_pool, k_scale, v_scale, idx_k_pool, block_table
         idx = "nvfp4" if idx_k_scale is not None else "fp8"
     p = problem(B, decode_query_len, int(q.shape[1]), int(k_pool.shape[1]),
                 int(idx_k_pool.shape[1]), int(block_table.shape[1]), int(k_pool.shape[0]),
-                kv_dtype=kv, idx_k_dtype=idx, topk=topk, sm_scale=sm_scale)
+                kv_dtype=kv, idx_k_dtype=idx, topk=topk, sm_scale=sm_scale, flags=flags)
     t = tensors(q, idx_q, k_pool, v_pool, k_scale, v_scale, idx_k_pool, block_table, ctx_lens,
                 idx_k_scale)
     return p, t
@@ -225,6 +233,13 @@ def msa_last_dispatch() -> str:
     n = _lib.msa_last_dispatch(None, 0)
     buf = ctypes.create_string_buffer(n + 1)
     _lib.msa_last_dispatch(buf, n + 1)
+    return buf.value.decode()
+
+
+def msa_last_check_failure() -> str:
+    n = _lib.msa_last_check_failure(None, 0)
+    buf = ctypes.create_string_buffer(n + 1)
+    _lib.msa_last_check_failure(buf, n + 1)
     return buf.value.decode()
 
 

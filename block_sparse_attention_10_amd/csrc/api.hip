@@ -12,6 +12,7 @@ namespace msa {
 
 static thread_local int g_last_hip_error = 0;
 static thread_local std::string g_last_dispatch;
+static thread_local std::string g_last_check_failure;
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -49,7 +50,7 @@ int check_problem(const msa_problem* p, Dims* d) {
     return MSA_ERR_INVALID_ARG;
   if (p->num_q_heads % p->num_kv_heads != 0) return MSA_ERR_INVALID_ARG;
   if (!(p->sm_scale >= 0.f) || !isfinite(p->sm_scale)) return MSA_ERR_INVALID_ARG;
-  if (p->flags != 0) return MSA_ERR_INVALID_ARG;
+  if ((p->flags & ~(uint32_t)MSA_FLAG_DEBUG_CHECKS) != 0) return MSA_ERR_INVALID_ARG;
   if (p->head_dim != 128 || p->idx_dim != 64 || p->block_size != 128 || p->page_size != 16 ||
       p->local_blocks != 1 || p->topk > 16 || p->decode_query_len > 16 ||
       p->num_idx_heads > 16 || p->num_q_heads / p->num_kv_heads > 16)
@@ -73,6 +74,7 @@ int check_problem(const msa_problem* p, Dims* d) {
   d->idx_dtype = p->idx_k_dtype;
   const float scale = p->sm_scale > 0.f ? p->sm_scale : 1.0f / sqrtf((float)p->head_dim);
   d->scale_log2 = scale * 1.4426950408889634f;
+  d->debug = (p->flags & MSA_FLAG_DEBUG_CHECKS) != 0;
   return MSA_OK;
 }
 
@@ -109,6 +111,26 @@ int hip_status(hipError_t e) {
   return MSA_ERR_HIP;
 }
 
+// With MSA_FLAG_DEBUG_CHECKS: checks the data-dependent inputs of a call
+// (synchronising `s`) and returns MSA_ERR_BAD_DATA, before any other launch,
+// when one is invalid.  Without the flag: nothing.
+int debug_checks(const Dims& d, const int32_t* ctx_lens, const int32_t* block_table,
+                 const int32_t* selected, const int32_t* page_table, bool new_tokens_only,
+                 hipStream_t s, std::string* note) {
+  if (!d.debug) return MSA_OK;
+  const CheckInputs a = {ctx_lens, block_table, selected, page_table, d.B, d.T, d.MAXB, d.NB,
+                         d.topk, new_tokens_only};
+  std::string failure;
+  const int e = hip_status(run_input_checks(a, s, &failure));
+  if (e) return e;
+  if (!failure.empty()) {
+    g_last_check_failure = failure;
+    return MSA_ERR_BAD_DATA;
+  }
+  *note += "input_checks[1x1024] ";
+  return MSA_OK;
+}
+
 }  // namespace
 }  // namespace msa
 
@@ -123,6 +145,9 @@ int msa_index_score(const msa_problem* p, const msa_tensors* t, float* block_sco
   if ((e = check_problem(p, &d))) return e;
   if ((e = check_index_inputs(d, t)) || (e = check_ptr(block_scores))) return e;
   std::string note;
+  if ((e = debug_checks(d, t->ctx_lens, t->block_table, nullptr, nullptr, false,
+                        (hipStream_t)stream, &note)))
+    return e;
   e = hip_status(launch_index_scan(d, t->idx_q, t->idx_k_pool, t->idx_k_scale, t->block_table,
                                    t->ctx_lens, block_scores, (hipStream_t)stream, &note));
   if (e == MSA_OK) g_last_dispatch = note;
@@ -138,6 +163,9 @@ int msa_select_blocks(const msa_problem* p, const float* block_scores, const int
       (e = check_ptr(n_selected)))
     return e;
   std::string note;
+  if ((e = debug_checks(d, ctx_lens, nullptr, nullptr, nullptr, false, (hipStream_t)stream,
+                        &note)))
+    return e;
   e = hip_status(launch_select(d, block_scores, ctx_lens, nullptr, selected, n_selected, nullptr,
                                (hipStream_t)stream, &note));
   if (e == MSA_OK) g_last_dispatch = note;
@@ -152,6 +180,9 @@ int msa_build_page_table(const msa_problem* p, const int32_t* selected,
   if ((e = check_ptr(selected)) || (e = check_ptr(block_table)) || (e = check_ptr(page_table)))
     return e;
   std::string note;
+  if ((e = debug_checks(d, nullptr, block_table, selected, nullptr, false, (hipStream_t)stream,
+                        &note)))
+    return e;
   e = hip_status(launch_page_table(d, selected, block_table, page_table, (hipStream_t)stream,
                                    &note));
   if (e == MSA_OK) g_last_dispatch = note;
@@ -176,6 +207,9 @@ int msa_sparse_decode(const msa_problem* p, const msa_tensors* t, const int32_t*
   if (workspace_bytes < w.total) return MSA_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
   std::string note;
+  if ((e = debug_checks(d, t->ctx_lens, nullptr, nullptr, page_table, false, (hipStream_t)stream,
+                        &note)))
+    return e;
   e = hip_status(launch_sparse_attention(d, t->q, t->k_pool, t->v_pool, t->k_scale, t->v_scale,
                                          page_table, t->ctx_lens,
                                          reinterpret_cast<float*>(ws + w.part_o),
@@ -205,6 +239,8 @@ int msa_decode(const msa_problem* p, const msa_tensors* t, int32_t* selected,
   int32_t* pt = page_table ? page_table : reinterpret_cast<int32_t*>(ws + w.page_table);
   hipStream_t s = (hipStream_t)stream;
   std::string note;
+  if ((e = debug_checks(d, t->ctx_lens, t->block_table, nullptr, nullptr, false, s, &note)))
+    return e;
   if ((e = hip_status(launch_index_scan(d, t->idx_q, t->idx_k_pool, t->idx_k_scale,
                                         t->block_table, t->ctx_lens, scores, s, &note))))
     return e;
@@ -242,6 +278,9 @@ int msa_insert_kv(const msa_problem* p, const msa_pools* pools, const int32_t* b
   const InsertPools pl = {pools->k_pool, pools->v_pool, pools->k_scale, pools->v_scale,
                           pools->idx_k_pool, pools->idx_k_scale};
   std::string note;
+  if ((e = debug_checks(d, ctx_lens, block_table, nullptr, nullptr, true, (hipStream_t)stream,
+                        &note)))
+    return e;
   e = hip_status(launch_insert(d, k_new, v_new, idx_k_new, block_table, ctx_lens, pl,
                                (hipStream_t)stream, &note));
   if (e == MSA_OK) g_last_dispatch = note;
@@ -255,11 +294,22 @@ const char* msa_status_string(int status) {
     case MSA_ERR_UNSUPPORTED: return "unsupported dtype or shape";
     case MSA_ERR_WORKSPACE: return "workspace too small";
     case MSA_ERR_HIP: return "HIP launch failed";
+    case MSA_ERR_BAD_DATA: return "input data failed a debug check";
     default: return "unknown status";
   }
 }
 
 int msa_last_hip_error(void) { return g_last_hip_error; }
+
+int msa_last_check_failure(char* buf, size_t n) {
+  const std::string& s = g_last_check_failure;
+  if (buf && n > 0) {
+    const size_t k = s.size() < n - 1 ? s.size() : n - 1;
+    memcpy(buf, s.data(), k);
+    buf[k] = '\0';
+  }
+  return (int)s.size();
+}
 
 int msa_last_dispatch(char* buf, size_t n) {
   const std::string& s = g_last_dispatch;

@@ -16,6 +16,7 @@ struct Dims {
   int B, T, Hq, Hkv, Hidx, MAXB, NB, topk;
   int kv_dtype, idx_dtype;
   float scale_log2;  // softmax scale * log2(e)
+  bool debug;        // MSA_FLAG_DEBUG_CHECKS
   int R() const { return B * T; }
   int G() const { return Hq / Hkv; }
   int PT() const { return topk * 8; }  // page-table row length
@@ -71,5 +72,19 @@ hipError_t launch_insert(const Dims& d, const void* k_new, const void* v_new,
                          std::string* note);
 
 hipError_t launch_selftest_decoders(float* out, hipStream_t s);
+
+// Data-dependent inputs one call reads (NULL: not read by that call).
+struct CheckInputs {
+  const int32_t* ctx_lens;
+  const int32_t* block_table;
+  const int32_t* selected;
+  const int32_t* page_table;
+  int B, T, MAXB, NB, topk;
+  bool new_tokens_only;  // table entries of the T newest tokens' blocks only
+};
+
+// Runs the input checks on `s`, waits for them, and leaves in `failure` a
+// description of the first violation ("" when the inputs are valid).
+hipError_t run_input_checks(const CheckInputs& a, hipStream_t s, std::string* failure);
 
 }  // namespace msa

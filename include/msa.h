@@ -69,9 +69,19 @@
  *    MSA_ERR_UNSUPPORTED for a dtype or shape outside the list above;
  *    MSA_ERR_WORKSPACE for a workspace smaller than msa_workspace_bytes();
  *    MSA_ERR_HIP when a launch failed (msa_last_hip_error() gives the HIP
- *    code).  No exception crosses this boundary.  Data-dependent faults
- *    (ctx_lens outside the bounds above, block_table entries >= NB) are not
- *    checked on the device and are undefined behaviour.
+ *    code); MSA_ERR_BAD_DATA when a debug check failed (below).  No
+ *    exception crosses this boundary.
+ *  - Data-dependent inputs (ctx_lens outside the bounds above, block_table
+ *    entries outside [0, NB), selections or page tables not of the form
+ *    described) are not checked by default and are undefined behaviour.
+ *    With flags = MSA_FLAG_DEBUG_CHECKS every call first checks, on the
+ *    device, the ctx_lens, block_table entries, selected ids and page-table
+ *    rows it reads (for the write path: the table entries of the new
+ *    tokens' blocks; elsewhere every block of the context), waits for that
+ *    check (the call synchronises `stream`, so it cannot be captured into a
+ *    graph), and returns MSA_ERR_BAD_DATA without launching anything else
+ *    when an input is invalid; msa_last_check_failure() names the first
+ *    offending entry.  Checks of calls on one device are serialised.
  *  - Calls on different streams must use distinct workspaces and outputs.
  */
 #ifndef MSA_H_
@@ -89,8 +99,12 @@ enum {
   MSA_ERR_INVALID_ARG = -1,
   MSA_ERR_UNSUPPORTED = -2,
   MSA_ERR_WORKSPACE = -3,
-  MSA_ERR_HIP = -4
+  MSA_ERR_HIP = -4,
+  MSA_ERR_BAD_DATA = -5
 };
+
+/* msa_problem.flags */
+enum { MSA_FLAG_DEBUG_CHECKS = 1 };
 
 enum { MSA_DTYPE_BF16 = 0, MSA_DTYPE_FP8_E4M3 = 1, MSA_DTYPE_NVFP4 = 2 };
 
@@ -112,7 +126,7 @@ typedef struct msa_problem {
   int32_t kv_dtype;           /* MSA_DTYPE_BF16 / _FP8_E4M3 / _NVFP4          */
   int32_t idx_k_dtype;        /* MSA_DTYPE_BF16 / _FP8_E4M3 / _NVFP4          */
   float sm_scale;             /* softmax scale; 0 means 1/sqrt(head_dim)      */
-  uint32_t flags;             /* reserved, must be 0                          */
+  uint32_t flags;             /* 0 or MSA_FLAG_DEBUG_CHECKS                   */
 } msa_problem;
 
 typedef struct msa_tensors {
@@ -226,6 +240,12 @@ const char* msa_status_string(int status);
 
 /* HIP error code of the last MSA_ERR_HIP on the calling thread (0 if none). */
 int msa_last_hip_error(void);
+
+/* Describes the first invalid input found by the debug checks of the
+ * calling thread's last call that returned MSA_ERR_BAD_DATA (which entry,
+ * its value and the rule it breaks).  Copies at most n - 1 bytes plus a
+ * terminating NUL into buf; returns the full length (0 if none). */
+int msa_last_check_failure(char* buf, size_t n);
 
 /* Names the kernels and launch shapes the calling thread's last successful
  * call enqueued (what was executed, not just configured).  Copies at most

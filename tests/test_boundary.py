@@ -62,7 +62,8 @@ def good(**kw):
     (dict(num_q_heads=8, num_kv_heads=3), msa.MSA_ERR_INVALID_ARG),
     (dict(sm_scale=-1.0), msa.MSA_ERR_INVALID_ARG),
     (dict(sm_scale=float("nan")), msa.MSA_ERR_INVALID_ARG),
-    (dict(flags=1), msa.MSA_ERR_INVALID_ARG),
+    (dict(flags=2), msa.MSA_ERR_INVALID_ARG),
+    (dict(flags=msa.MSA_FLAG_DEBUG_CHECKS | 4), msa.MSA_ERR_INVALID_ARG),
     (dict(head_dim=64), msa.MSA_ERR_UNSUPPORTED),
     (dict(idx_dim=128), msa.MSA_ERR_UNSUPPORTED),
     (dict(block_size=64), msa.MSA_ERR_UNSUPPORTED),
@@ -138,9 +139,21 @@ def test_workspace_grows_with_the_problem():
     assert big > small
 
 
+def test_debug_flag_is_accepted_and_checked_after_the_arguments():
+    # the debug checks run only once the host-side validation passed: a bad
+    # argument is still reported as such, with no launch
+    p = good(flags=msa.MSA_FLAG_DEBUG_CHECKS)
+    assert msa.msa_workspace_bytes(p) == msa.msa_workspace_bytes(good())
+    L = msa.lib()
+    t = msa.Tensors()
+    assert L.msa_index_score(ctypes.byref(p), ctypes.byref(t), None, None) == \
+        msa.MSA_ERR_INVALID_ARG
+    assert msa.msa_last_check_failure() == ""
+
+
 def test_status_strings():
     assert msa.msa_status_string(0) == "ok"
-    for c in (-1, -2, -3, -4):
+    for c in (-1, -2, -3, -4, -5):
         assert msa.msa_status_string(c) != "unknown status"
     assert msa.msa_status_string(7) == "unknown status"
 
