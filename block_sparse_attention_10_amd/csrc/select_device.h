@@ -8,14 +8,18 @@
 // section 2: one workgroup per request covers all draft positions.
 //
 // Design: a row's candidates are spread over 1, 2 or 4 waves (4 / T when
-// T < 4).  Every lane streams its candidates in ascending id order into a
-// register-resident sorted list of the topk - 1 best 64-bit keys (orderable
-// score << 32 | ~id, so a larger key is a better block and equal scores
-// favour the lower id).  Each wave then pops its topk - 1 best keys by
-// repeated wave maxima (DPP reductions, no LDS traffic), the waves of a row
-// meet in LDS, and one wave ranks the union (at most 60 finalists, one per
-// lane), sorts the winners by id and writes the row's selection and page
-// table.
+// T < 4) and compared as 64-bit keys (orderable score << 32 | ~id, so a
+// larger key is a better block and equal scores favour the lower id).  Each
+// lane folds its candidates into its best key; the K1-th best lane maximum
+// of a wave (K1 = topk - 1) has K1 real candidates at or above it, so only
+// candidates reaching the largest such bound of the row's waves can be among
+// the K1 best.  Those survivors (typically a few dozen) are gathered in LDS
+// and ranked by counting; the winners are ordered by id.  A row with more
+// survivors than LDS holds (a few lanes owning most of the best keys) falls
+// back to per-lane sorted lists, wave-max pops and a merge-rank.  The kernel
+// runs each path about once per launch, so code size (instruction fetch)
+// counts as much as instruction count: loops stop at the wave's real
+// candidate count instead of being duplicated per case.
 #pragma once
 
 #include "msa_device.h"
@@ -80,11 +84,64 @@ __device__ __forceinline__ int key_id(uint64_t k) {
   return (int)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFu));
 }
 
-// LDS a selecting workgroup needs.
+constexpr int kCap = 128;  // survivors of the threshold a row can rank (2 per lane)
+
+// LDS a selecting workgroup needs.  Row slot q of a pass is served by waves
+// q * parts .. q * parts + parts - 1.
 struct SelectLds {
-  uint64_t finalists[4 * kList];  // wave w's picks at [w * K1, w * K1 + K1)
+  uint64_t survivors[4][kCap];    // keys at or above the row's threshold
+  uint64_t finalists[4 * kList];  // list path: wave w's picks at [w * K1, w * K1 + K1)
+  uint64_t bound[4];              // per wave: its K1-th best lane maximum, or 0
+  int32_t count[4];               // survivors per row slot
   int32_t row_sel[4][kMaxTopk];
 };
+
+// Batch slots (of kBatch) the wave needs for the candidates c0, c0 + stride,
+// ... below `local`, for lane `lane` (lanes of a wave start at most 63
+// apart, so lane 0's count covers every lane).
+__device__ __forceinline__ int wave_slots(int c0, int lane, int stride, int local) {
+  const int c0min = c0 - lane;
+  if (local <= c0min) return 0;
+  return min(kBatch, (local - c0min + stride - 1) / stride);
+}
+
+__device__ __forceinline__ uint64_t key_of(uint32_t ord, int c) {
+  return ((uint64_t)ord << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)c);
+}
+
+// Orderable scores of a batch (ok, 0 past `local`: below every real key)
+// folded into the lane's best key.  `nw`: the wave's slots.
+__device__ __forceinline__ void key_batch(uint32_t (&ok)[kBatch], const float (&sv)[kBatch],
+                                          uint64_t& best, int c0, int stride, int local,
+                                          int nw) {
+#pragma unroll
+  for (int u = 0; u < kBatch; ++u) {
+    if (u >= nw) break;  // wave-uniform
+    const int c = c0 + u * stride;
+    const uint32_t o = c < local ? orderable(sv[u]) : 0u;
+    ok[u] = o;
+    const uint64_t x = key_of(o, c);
+    if (o != 0 && x > best) best = x;
+  }
+}
+
+// Counts (WRITE false) or stores at out[0 .. room) (WRITE true) the keys of
+// a batch that reach `bound`; returns how many reach it.
+template <bool WRITE>
+__device__ __forceinline__ int pass_keys(const uint32_t (&ok)[kBatch], int c0, int stride,
+                                         uint64_t bound, int nw, uint64_t* out, int room) {
+  int n = 0;
+#pragma unroll
+  for (int u = 0; u < kBatch; ++u) {
+    if (u >= nw) break;  // wave-uniform
+    const uint64_t x = key_of(ok[u], c0 + u * stride);
+    if (ok[u] != 0 && x >= bound) {
+      if (WRITE && n < room) out[n] = x;
+      ++n;
+    }
+  }
+  return n;
+}
 
 // Inserts a batch of candidates (ids c0, c0 + stride, ...; those >= local
 // are skipped) into the lane's descending list of kList keys.
@@ -107,9 +164,42 @@ __device__ __forceinline__ void insert_batch(uint64_t (&list)[kList], const floa
   }
 }
 
+// Loads the batch of candidates c0, c0 + stride, ... below `local` (0 past it).
+__device__ __forceinline__ void load_batch(float (&sv)[kBatch], const float* srow, int c0,
+                                           int stride, int local) {
+#pragma unroll
+  for (int u = 0; u < kBatch; ++u) {
+    const int c = c0 + u * stride;
+    sv[u] = c < local ? srow[c] : 0.f;
+  }
+}
+
+// Lane j's value of a 64-bit key.
+__device__ __forceinline__ uint64_t lane_key(uint64_t v, int j) {
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), j);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, j);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Number of set bits of `m` in lanes below this one.
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
 // Selection (and, when page_table is given, the page table) for every row of
 // request b.  Called by all 256 threads of a 4-wave workgroup; contains
 // workgroup barriers.
+//
+// Per row: every lane takes the best key among its candidates; each wave
+// finds the K1-th best of its lane maxima (K1 = topk - 1) by counting.  That key has
+// K1 real candidates at or above it, so no candidate below the largest of
+// the row's wave bounds can be among the K1 best: only candidates reaching
+// it survive (typically a few dozen), gathered in LDS and ranked by
+// counting.  Rows with more than kCap survivors (a few lanes holding most of
+// the best keys) take the list path instead: per-lane sorted lists of the
+// K1 best keys, K1 wave-max pops per wave, and a merge-rank of the waves'
+// picks.
 __device__ __forceinline__ void select_request(int b, const float* __restrict__ scores,
                                             const int32_t* __restrict__ ctx_lens,
                                             const int32_t* __restrict__ block_table,
@@ -117,8 +207,6 @@ __device__ __forceinline__ void select_request(int b, const float* __restrict__ 
                                             int32_t* __restrict__ n_selected,
                                             int32_t* __restrict__ page_table, int T, int MAXB,
                                             int topk, SelectLds& sh) {
-  uint64_t* finalists = sh.finalists;
-  auto& row_sel = sh.row_sel;
   const int lane = lane_id();
   const int wave = wave_id();
   const int parts = T >= 4 ? 1 : (T == 1 ? 4 : (T == 2 ? 2 : 1));
@@ -126,10 +214,12 @@ __device__ __forceinline__ void select_request(int b, const float* __restrict__ 
   const int K1 = topk - 1;
   const int stride = parts * kWave;
   const int part = wave % parts;
+  const int slot = wave / parts;
   const int cfirst = part * kWave + lane;
+  auto& row_sel = sh.row_sel;
 
   for (int t0 = 0; t0 < T; t0 += rows_per_pass) {
-    const int t = t0 + wave / parts;
+    const int t = t0 + slot;
     // The first batch of scores is loaded together with the context length
     // (indices clamped into the row, rows into the request), so the two
     // round trips overlap; the empty asm pins the loads ahead of the branches
@@ -150,28 +240,117 @@ __device__ __forceinline__ void select_request(int b, const float* __restrict__ 
     const int pos = L - T + t;
     const int local = pos >> 7;
     const bool take_all = local + 1 <= topk;
+    // uniform over the row's waves
+    const bool work = active && !take_all && K1 > 0;
+    if (part == 0 && lane == 0) sh.count[slot] = 0;
 
-    if (active && !take_all && K1 > 0) {
+    // lane maxima; the orderable scores of the first two batches stay in
+    // registers
+    float sv2[kBatch];
+    uint32_t ok0[kBatch], ok1[kBatch];
+    const int c1 = cfirst + kBatch * stride;
+    const int c2 = c1 + kBatch * stride;
+    const int nw0 = wave_slots(cfirst, lane, stride, local);
+    const int nw1 = wave_slots(c1, lane, stride, local);
+    uint64_t lmax = 0;  // 0 ranks below every real key
+    if (work) {
+      if (nw1 > 0) load_batch(sv2, srow, c1, stride, local);
+      key_batch(ok0, sv, lmax, cfirst, stride, local, nw0);
+      if (nw1 > 0) key_batch(ok1, sv2, lmax, c1, stride, local, nw1);
+      for (int c0 = c2; c0 - lane < local; c0 += kBatch * stride) {  // wave-uniform
+        float sx[kBatch];
+        uint32_t okx[kBatch];
+        load_batch(sx, srow, c0, stride, local);
+        key_batch(okx, sx, lmax, c0, stride, local, wave_slots(c0, lane, stride, local));
+      }
+    }
+    // this wave's K1-th best lane maximum (0 when fewer lanes have one):
+    // the lane with exactly K1 - 1 better maxima holds it (keys are unique)
+    uint64_t wbound = 0;
+    if (work) {
+      int above = 0;
+#pragma unroll
+      for (int j = 0; j < kWave; ++j) above += lane_key(lmax, j) > lmax ? 1 : 0;
+      const uint64_t at = __ballot(lmax != 0 && above == K1 - 1);
+      if (at) wbound = lane_key(lmax, __builtin_ctzll(at));
+    }
+    if (lane == 0) sh.bound[wave] = wbound;
+    __syncthreads();
+
+    // survivors: keys at or above the largest bound of the row's waves
+    uint64_t bound = 0;
+    for (int q = 0; q < parts; ++q) {
+      const uint64_t x = sh.bound[slot * parts + q];
+      bound = x > bound ? x : bound;
+    }
+    if (work) {
+      int mine = pass_keys<false>(ok0, cfirst, stride, bound, nw0, nullptr, 0) +
+                 pass_keys<false>(ok1, c1, stride, bound, nw1, nullptr, 0);
+      for (int c0 = c2; c0 - lane < local; c0 += kBatch * stride) {  // wave-uniform
+        float sx[kBatch];
+        uint32_t okx[kBatch];
+        uint64_t unused = 0;
+        const int nw = wave_slots(c0, lane, stride, local);
+        load_batch(sx, srow, c0, stride, local);
+        key_batch(okx, sx, unused, c0, stride, local, nw);
+        mine += pass_keys<false>(okx, c0, stride, bound, nw, nullptr, 0);
+      }
+      // this lane's offset among the wave's survivors, bit by bit
+      int below = 0, total = 0;
+      for (int bit = 0; bit < 31; ++bit) {
+        if (__ballot((mine >> bit) != 0) == 0) break;  // wave-uniform
+        const uint64_t mb = __ballot((mine >> bit) & 1);
+        below += lanes_below(mb) << bit;
+        total += __popcll(mb) << bit;
+      }
+      int base = 0;
+      if (lane == 0 && total > 0) base = atomicAdd(&sh.count[slot], total);
+      base = __shfl(base, 0) + below;
+      if (mine > 0 && base < kCap) {
+        uint64_t* out = sh.survivors[slot] + base;
+        int room = kCap - base;
+        const int n0 = pass_keys<true>(ok0, cfirst, stride, bound, nw0, out, room);
+        out += n0;
+        room -= n0;
+        if (room > 0) {
+          const int n1 = pass_keys<true>(ok1, c1, stride, bound, nw1, out, room);
+          out += n1;
+          room -= n1;
+        }
+        for (int c0 = c2; c0 < local && room > 0; c0 += kBatch * stride) {
+          float sx[kBatch];
+          uint32_t okx[kBatch];
+          uint64_t unused = 0;
+          const int nw = wave_slots(c0, lane, stride, local);
+          load_batch(sx, srow, c0, stride, local);
+          key_batch(okx, sx, unused, c0, stride, local, nw);
+          const int n = pass_keys<true>(okx, c0, stride, bound, nw, out, room);
+          out += n;
+          room -= n;
+        }
+      }
+    }
+    __syncthreads();
+    const int m = sh.count[slot];
+    const bool list_path = work && m > kCap;  // uniform over the row's waves
+
+    if (list_path) {
       uint64_t list[kList];
 #pragma unroll
-      for (int j = 0; j < kList; ++j) list[j] = 0;  // 0 ranks below every real key
-      insert_batch(list, sv, cfirst, stride, local);
-      for (int c0 = cfirst + kBatch * stride; c0 < local; c0 += kBatch * stride) {
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-          const int c = c0 + u * stride;
-          sv[u] = c < local ? srow[c] : 0.f;
-        }
-        insert_batch(list, sv, c0, stride, local);
+      for (int j = 0; j < kList; ++j) list[j] = 0;
+      for (int c0 = cfirst; c0 < local; c0 += kBatch * stride) {
+        float sx[kBatch];
+        load_batch(sx, srow, c0, stride, local);
+        insert_batch(list, sx, c0, stride, local);
       }
       // this wave's K1 best keys, best first; 0 once its lists run dry
       for (int k = 0; k < K1; ++k) {
         const uint64_t best = wave_max_u64(list[0]);
         if (best == 0) {  // wave-uniform
-          for (int e = lane; e < K1 - k; e += kWave) finalists[wave * K1 + k + e] = 0;
+          for (int e = lane; e < K1 - k; e += kWave) sh.finalists[wave * K1 + k + e] = 0;
           break;
         }
-        if (lane == 0) finalists[wave * K1 + k] = best;
+        if (lane == 0) sh.finalists[wave * K1 + k] = best;
         if (list[0] == best) {
 #pragma unroll
           for (int j = 0; j < kList - 1; ++j) list[j] = list[j + 1];
@@ -190,33 +369,46 @@ __device__ __forceinline__ void select_request(int b, const float* __restrict__ 
         if (lane == 0) row_sel[wave][0] = local;
         n = 1;
       } else {
-        // rank the union of this row's per-wave picks (waves wave ..
-        // wave + parts - 1, stored contiguously).  Each wave's list is sorted
-        // best first (pop order, zeros last) and keys are unique, so a pick's
-        // rank is its index plus, per other list, the count of better keys
-        // there (a binary search).
-        const int m = parts * K1;
-        const uint64_t* fin = finalists + wave * K1;
-        const uint64_t mine = lane < m ? fin[lane] : 0;
-        const int own = lane < m ? lane / K1 : 0;
-        int rank = lane - own * K1;
-        for (int w = 0; w < parts; ++w) {  // wave-uniform
-          if (w == own) continue;
-          const uint64_t* list = fin + w * K1;
-          int cnt = 0;
+        if (!list_path) {
+          uint64_t* sv_ = sh.survivors[slot];
+          const uint64_t e0 = lane < m ? sv_[lane] : 0;
+          const uint64_t e1 = lane + kWave < m ? sv_[lane + kWave] : 0;
+          if (lane < 8 && m + lane < kCap) sv_[m + lane] = 0;
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          int r0 = 0, r1 = 0;
+          for (int j = 0; j < m; j += 8) {
 #pragma unroll
-          for (int step = 8; step >= 1; step >>= 1)
-            if (cnt + step <= K1 && list[cnt + step - 1] > mine) cnt += step;
-          rank += cnt;
+            for (int q = 0; q < 8; ++q) {
+              const uint64_t x = sv_[j + q];
+              r0 += x > e0 ? 1 : 0;
+              r1 += x > e1 ? 1 : 0;
+            }
+          }
+          if (lane < m && r0 < K1) row_sel[wave][r0] = key_id(e0);
+          if (lane + kWave < m && r1 < K1) row_sel[wave][r1] = key_id(e1);
+        } else {
+          const int mf = parts * K1;
+          const uint64_t* fin = sh.finalists + wave * K1;
+          const uint64_t mine = lane < mf ? fin[lane] : 0;
+          const int own = lane < mf ? lane / K1 : 0;
+          int rank = lane - own * K1;
+          for (int w = 0; w < parts; ++w) {
+            if (w == own) continue;
+            const uint64_t* list = fin + w * K1;
+            int cnt = 0;
+#pragma unroll
+            for (int step = 8; step >= 1; step >>= 1)
+              if (cnt + step <= K1 && list[cnt + step - 1] > mine) cnt += step;
+            rank += cnt;
+          }
+          if (lane < mf && rank < K1 && mine != 0) row_sel[wave][rank] = key_id(mine);
         }
-        const bool win = lane < m && rank < K1 && mine != 0;
-        const int id = key_id(mine);
-        // position among the winners by ascending id
-        __builtin_amdgcn_wave_barrier();
-        if (win) row_sel[wave][rank] = id;
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int id = lane < K1 ? row_sel[wave][lane] : INT32_MAX;
         int posn = 0;
 #pragma unroll
         for (int e = 0; e < kList; ++e) {
@@ -225,7 +417,7 @@ __device__ __forceinline__ void select_request(int b, const float* __restrict__ 
         }
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if (win) row_sel[wave][posn] = id;
+        if (lane < K1) row_sel[wave][posn] = id;
         if (lane == 0) row_sel[wave][K1] = local;
         n = topk;
       }

@@ -10,15 +10,10 @@
 // to its physical block and expanded to 8 page ids of 16 tokens; KV stays in
 // place, only this table is rebuilt.
 //
-// Design: one 256-thread workgroup per request.  A row's candidates are
-// spread over 1, 2 or 4 waves (4 / T when T < 4).  Every lane streams its
-// candidates in ascending id order into a register-resident sorted list of
-// the topk - 1 best 64-bit keys (orderable score << 32 | ~id, so a larger
-// key is a better block and equal scores favour the lower id).  The wave
-// then pops its topk - 1 best keys by repeated wave maxima (DPP reductions,
-// no LDS traffic), the waves of a row meet in LDS, and one wave ranks the
-// union (at most 60 finalists, one per lane), sorts the winners by id and
-// writes the row's selection and page table.
+// Design: one 256-thread workgroup per request; the selection itself (a
+// threshold that leaves a few dozen candidates per row, ranked by counting
+// in LDS, with a per-lane sorted-list path as the fallback) is described in
+// select_device.h.
 #include "msa_device.h"
 #include "msa_internal.h"
 #include "select_device.h"
