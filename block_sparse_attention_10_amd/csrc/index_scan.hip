@@ -7,10 +7,10 @@
 // MI355X article, section 2: one indexer pass per request covers every draft
 // position, so each key load is reused by all T rows.
 //
-// Design (gfx950): this is a matrix-vector stream, not a dense contraction,
-// so it runs on the VALU.  One wave scores one logical block for all rows of
-// its request: every load instruction moves 1 KB of contiguous keys (64
-// lanes x 16 B); bf16 keys feed v_dot2_f32_bf16 directly, fp8 keys are
+// Design (gfx950): for a single row this is a matrix-vector stream, not a
+// dense contraction, so it runs on the VALU.  One wave scores one logical
+// block for all rows of its request: every load instruction moves 1 KB of
+// contiguous keys (64 lanes x 16 B); bf16 keys feed v_dot2_f32_bf16 directly, fp8 keys are
 // widened to bf16 pairs in registers first.  4-bit keys (E2M1 codes, one
 // E4M3 scale per 16 dims, the NVFP4 layout of the aisoku.org article,
 // section "何が新しいか") are widened to unscaled bf16 pairs, dotted with the
@@ -19,7 +19,9 @@
 // power-of-two scales) every fp32 partial sum is exact in any order.  The
 // lanes that share a token are folded by a transpose-reduce (each butterfly
 // stage halves the partials a lane carries), then the wave takes the causal
-// max.
+// max.  Requests with several rows (speculative verification) multiply the
+// VALU work per byte; from a few rows on, the dot products move to the
+// matrix cores with the rows as the M dimension (scan_block_mfma).
 #include "msa_device.h"
 #include "msa_internal.h"
 
@@ -206,8 +208,110 @@ __device__ __forceinline__ void scan_block(const uint16_t* __restrict__ idx_q,
   }
 }
 
+// Max over the 16 lanes of each DPP row (lanes 16 r .. 16 r + 15), returned
+// to all of them: quad swaps, then half-row and row mirrors.
+__device__ __forceinline__ float row16_max(float v) {
+  v = dpp_max_step<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  v = dpp_max_step<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  v = dpp_max_step<0x141, 0xF>(v);  // row_half_mirror
+  return dpp_max_step<0x140, 0xF>(v);  // row_mirror
+}
+
+// The same scores on the matrix cores, for requests with several rows
+// (speculative verification): per index head, S = Q K^T with the request's
+// rows as the M dimension (T <= 16, zero rows beyond T) and the block's
+// tokens as N, 16 tokens per tile, on v_mfma_f32_16x16x32_bf16.  Lane l
+// supplies row / token l % 16 and the dims of k-group l / 16 (bf16 keys:
+// dims 32 s + 8 g .. + 7 of step s; fp8 keys: one 16-byte load of dims
+// 16 g .. 16 g + 15, split over the two steps and widened to bf16 exactly);
+// it receives rows 4 g .. 4 g + 3 of token l % 16.  Summing over heads in
+// the accumulators and taking the causal max per row over the tiles and the
+// 16 lanes of a DPP row gives the block score.  Products of bf16 values are
+// exact in fp32 and the synthetic sums stay below 2^24, so the scores equal
+// the VALU path's bit for bit.
+template <int KIND>
+__device__ __forceinline__ void scan_block_mfma(const uint16_t* __restrict__ idx_q,
+                                                const uint8_t* __restrict__ idx_k,
+                                                int phys_block, float* __restrict__ scores,
+                                                int b, int c, int L, int T, int Hidx, int MAXB,
+                                                int lane) {
+  static_assert(KIND == kBf16 || KIND == kFp8, "matrix-core scan: bf16 or fp8 keys");
+  constexpr int TB = KIND == kBf16 ? 128 : 64;  // bytes per token and head
+  constexpr int NL = KIND == kBf16 ? 2 : 1;     // 16-byte loads per token and lane
+  const int n = lane & 15, g = lane >> 4;
+  const size_t head_bytes = (size_t)kBlock * TB;
+  const uint8_t* kblk = idx_k + (size_t)phys_block * Hidx * head_bytes;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+
+  f32x4 acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int h = 0; h < Hidx; ++h) {
+    const uint8_t* kh = kblk + (size_t)h * head_bytes;
+    u32x4 kv[8][NL];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint8_t* kt = kh + (size_t)(16 * i + n) * TB;
+      if constexpr (KIND == kBf16) {
+        kv[i][0] = ldg128_stream(kt + 16 * g);
+        kv[i][1] = ldg128_stream(kt + 64 + 16 * g);
+      } else {
+        kv[i][0] = ldg128_stream(kt + 16 * g);
+      }
+    }
+    // row n of the request (zeros past T), the dims of this lane's k-group
+    u32x4 qa[2] = {zero, zero};
+    if (n < T) {
+      const uint16_t* qp = idx_q + ((size_t)(b * T + n) * Hidx + h) * kIdxDim;
+      if constexpr (KIND == kBf16) {
+        qa[0] = ldg128(qp + 8 * g);
+        qa[1] = ldg128(qp + 32 + 8 * g);
+      } else {
+        qa[0] = ldg128(qp + 16 * g);
+        qa[1] = ldg128(qp + 16 * g + 8);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        u32x4 kb;
+        if constexpr (KIND == kBf16) {
+          kb = kv[i][st];
+        } else {
+          const uint32_t lo = st ? kv[i][0].z : kv[i][0].x;
+          const uint32_t hi = st ? kv[i][0].w : kv[i][0].y;
+          kb.x = e4m3x2_to_bf16x2<false>(lo);
+          kb.y = e4m3x2_to_bf16x2<true>(lo);
+          kb.z = e4m3x2_to_bf16x2<false>(hi);
+          kb.w = e4m3x2_to_bf16x2<true>(hi);
+        }
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[st]),
+                                                         __builtin_bit_cast(bf16x8, kb), acc[i],
+                                                         0, 0, 0);
+      }
+    }
+  }
+
+  // rows 4 g + j: max over this lane's causal tokens 16 i + n, then over the
+  // 16 lanes of the DPP row
+  float* srow = scores + (size_t)b * T * MAXB + c;
+  const int tok0 = c * kBlock + n;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = 4 * g + j;
+    const int pos = L - T + row;
+    float best = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (tok0 + 16 * i <= pos) best = fmaxf(best, acc[i][j]);
+    best = row16_max(best);
+    if (n == 0 && row < T) srow[(size_t)row * MAXB] = best;
+  }
+}
+
 // msa_index_score: one wave per (request, logical block); blocks past the
-// context score -inf for every row.
+// context score -inf for every row.  TR 0: the matrix-core path.
 template <int KIND, int TR>
 __global__ __launch_bounds__(256) void index_scan_kernel(
     const uint16_t* __restrict__ idx_q, const uint8_t* __restrict__ idx_k,
@@ -229,7 +333,10 @@ __global__ __launch_bounds__(256) void index_scan_kernel(
     for (int t = lane; t < T; t += kWave) srow[(size_t)t * MAXB] = -INFINITY;
     return;
   }
-  scan_block<KIND, TR>(idx_q, idx_k, idx_ks, phys, scores, b, c, L, T, Hidx, MAXB, lane);
+  if constexpr (TR == 0)
+    scan_block_mfma<KIND>(idx_q, idx_k, phys, scores, b, c, L, T, Hidx, MAXB, lane);
+  else
+    scan_block<KIND, TR>(idx_q, idx_k, idx_ks, phys, scores, b, c, L, T, Hidx, MAXB, lane);
 }
 
 // Workgroups per CU that a scan launch lets run at once.  The kernel uses
@@ -246,6 +353,17 @@ size_t scan_lds_bytes(int kind, unsigned workgroups) {
   return kLdsPerCu / (workgroups >= 8192 ? 3 : 4);
 }
 
+// Requests with at least this many rows score on the matrix cores.
+// Measured on MI355X (scan of a 128-request fp8 layer, 8-16K contexts):
+// fp8 keys 17.5 vs 26.5 us at 3 rows, 17.8 vs 27.4 at 4, on par at 2; bf16
+// keys (32 requests, 32K) lose at 2 and 4 rows (26.0 vs 21.5, 26.4 vs 24.6:
+// a 128-byte key row spans two of the operand's load instructions) and win
+// from 8 (26.8 vs 42.2), where the row passes of the VALU path multiply.
+// The matrix-core launches run best uncapped (fp8, 4 rows: 17.8 us, 27.6
+// with 3 workgroups per CU).
+constexpr int kMfmaMinRowsBf16 = 5;
+constexpr int kMfmaMinRowsFp8 = 2;
+
 template <int KIND>
 hipError_t launch_kind(const Dims& d, const void* idx_q, const void* idx_k, const void* idx_ks,
                        const int32_t* bt, const int32_t* cl, float* scores, hipStream_t s,
@@ -255,20 +373,28 @@ hipError_t launch_kind(const Dims& d, const void* idx_q, const void* idx_k, cons
   const auto* q = static_cast<const uint16_t*>(idx_q);
   const auto* k = static_cast<const uint8_t*>(idx_k);
   const auto* ks = static_cast<const uint8_t*>(idx_ks);
-  const int tr = d.T == 1 ? 1 : (d.T == 2 ? 2 : 4);
-  const size_t lds = scan_lds_bytes(KIND, grid.x);
+  const bool mfma = (KIND == kBf16 && d.T >= kMfmaMinRowsBf16) ||
+                    (KIND == kFp8 && d.T >= kMfmaMinRowsFp8);
+  const int tr = mfma ? 0 : (d.T == 1 ? 1 : (d.T == 2 ? 2 : 4));
+  const size_t lds = mfma ? 0 : scan_lds_bytes(KIND, grid.x);
+  if constexpr (KIND != kFp4) {
+    if (tr == 0)
+      hipLaunchKernelGGL((index_scan_kernel<KIND, 0>), grid, block, lds, s, q, k, ks, bt, cl,
+                         scores, d.B, d.T, d.Hidx, d.MAXB);
+  }
   if (tr == 1)
     hipLaunchKernelGGL((index_scan_kernel<KIND, 1>), grid, block, lds, s, q, k, ks, bt, cl, scores,
                        d.B, d.T, d.Hidx, d.MAXB);
   else if (tr == 2)
     hipLaunchKernelGGL((index_scan_kernel<KIND, 2>), grid, block, lds, s, q, k, ks, bt, cl, scores,
                        d.B, d.T, d.Hidx, d.MAXB);
-  else
+  else if (tr == 4)
     hipLaunchKernelGGL((index_scan_kernel<KIND, 4>), grid, block, lds, s, q, k, ks, bt, cl, scores,
                        d.B, d.T, d.Hidx, d.MAXB);
   static const char* names[3] = {"bf16", "fp8", "nvfp4"};
   if (note)
-    *note += std::string("index_scan<") + names[KIND] + ",rows" + std::to_string(tr) +
+    *note += std::string("index_scan<") + names[KIND] +
+             (tr == 0 ? std::string(",mfma") : ",rows" + std::to_string(tr)) +
              ">[grid=" + std::to_string(grid.x) + "x256,lds=" + std::to_string(lds) + "]";
   return hipGetLastError();
 }
