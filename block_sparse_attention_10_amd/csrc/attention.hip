@@ -313,20 +313,29 @@ __global__ __launch_bounds__(64 * W, 4) void sparse_attn_kernel(
 
   uint8_t* stage = smem + wave * kWaveLds;
   const int nchunks = 4 * nblk;  // 4 chunks of 32 keys per block
-  for (int ci = split + S * wave; ci < nchunks; ci += S * W) {
+  // Chunks past the row's position (the tail of its local block, which
+  // comes last) are never visited: the loop stops at `limit` instead of
+  // skipping them, which measured faster (128K layer 43.6 vs 45.8 us).
+  const int limit = min(nchunks, 4 * (nblk - 1) + (vloc + 31) / 32);
+  // the registers of chunk ci (two pages); returns its first key row
+  auto load_chunk = [&](Chunk<KV> (&ch)[2], int ci) {
     const int u = ci >> 2;         // block slot in the row's table
     const int pg0 = (ci & 3) * 2;  // first page of the chunk inside the block
-    const bool local = u == nblk - 1;
-    if (local && 32 * (ci & 3) >= vloc) continue;  // past the row's position
-    const int idx = 8 * u;                         // wave-uniform
+    const int idx = 8 * u;         // wave-uniform
     const int P = idx < kWave ? __builtin_amdgcn_readlane(pt_lo, idx)
                               : __builtin_amdgcn_readlane(pt_hi, idx - kWave);
     const int phys = min(max(P >> 3, 0), max_block);  // a bad table cannot leave the pools
     const size_t row0 = ((size_t)phys * Hkv + g) * 128 + (size_t)pg0 * 16;
-    Chunk<KV> ch[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
       load_page<KV, STREAM>(ch[j], k_pool, v_pool, k_scale, v_scale, row0 + 16 * j, lane);
+    return row0;
+  };
+  // the online-softmax update with chunk ci
+  auto body = [&](Chunk<KV> (&ch)[2], int ci, size_t row0) {
+    const int u = ci >> 2;
+    const int pg0 = (ci & 3) * 2;
+    const bool local = u == nblk - 1;
     if constexpr (KV == 0) {
 #pragma unroll
       for (int j = 0; j < 2; ++j)
@@ -413,6 +422,11 @@ __global__ __launch_bounds__(64 * W, 4) void sparse_attn_kernel(
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  for (int ci = split + S * wave; ci < limit; ci += S * W) {
+    Chunk<KV> ch[2];
+    const size_t row0 = load_chunk(ch, ci);
+    body(ch, ci, row0);
   }
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
