@@ -23,9 +23,11 @@
 //    the softmax statistics of a head never cross lane groups but four.
 //  * P V on the same MFMA as O^T = V^T P^T.  P^T is exactly the S^T
 //    accumulator layout (no shuffle); V^T needs a transpose, so the V pages
-//    are staged through LDS and read back column-wise (16-byte slots of a
-//    row are XOR-swizzled so the four lane groups of a read hit disjoint
-//    banks).  bf16 V goes from HBM to LDS with direct global-to-LDS loads
+//    are staged through LDS and read back column-wise: fp8 / 4-bit V (widened
+//    in registers) with gfx950's transposing LDS read (ds_read_b64_tr_b16,
+//    two per 8 keys x 16 dims operand), bf16 V (loaded straight into LDS)
+//    with 16-bit reads, which measured faster there.  The 16-byte slots of a
+//    row are XOR-swizzled so that each read spreads over the banks.  bf16 V goes from HBM to LDS with direct global-to-LDS loads
 //    and occupies no registers.  P is split into bf16 hi + lo halves (two
 //    MFMAs) so the weights keep ~16 bits.
 //  * fp8 K/V: e4m3 -> bf16 is exact; the per-token K scale multiplies the
@@ -59,6 +61,9 @@ constexpr int kWaitVmem = 0x0F70;
 constexpr int kNonTemporal = 2;
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 __device__ __forceinline__ float neg_inf() { return -INFINITY; }
 
@@ -69,10 +74,20 @@ __device__ __forceinline__ int kappa(int g4, int jj) {
 }
 
 // Staged V rows are 256 bytes of 16 slots of 8 dims.  Slot s of row k sits
-// at physical slot s ^ vswz(k), so that the 4 row groups one V^T read
-// touches (rows 4 g4 + c, see kappa) land on distinct banks.
-__device__ __forceinline__ int vswz(int k) { return 2 * ((k >> 2) & 3); }
-__device__ __forceinline__ int voff(int k, int slot) { return k * kVRow + 16 * (slot ^ vswz(k)); }
+// at physical slot s ^ vswz(k).  bf16 V (16-bit column reads): the 4 row
+// groups one V^T read touches (rows 4 g4 + c, see kappa) land on distinct
+// banks with 2 ((k / 4) mod 4).  fp8 / 4-bit V (transposing reads): one read
+// takes 32 bytes (one 16-dim block) from each of rows 0..15 (or 16..31) of
+// the chunk, and 2 (k mod 8) sends them to every 32-byte bank group exactly
+// twice.
+template <int KV>
+__device__ __forceinline__ int vswz(int k) {
+  return KV == 0 ? 2 * ((k >> 2) & 3) : 2 * (k & 7);
+}
+template <int KV>
+__device__ __forceinline__ int voff(int k, int slot) {
+  return k * kVRow + 16 * (slot ^ vswz<KV>(k));
+}
 
 template <int KV>
 struct Chunk {
@@ -140,15 +155,15 @@ __device__ __forceinline__ void load_page(Chunk<KV>& c, const uint8_t* __restric
 // bf16 V of one page straight from HBM into its LDS rows, no registers
 // involved.  Load i fills rows 4i..4i+3 (1 KB, 16 bytes per lane at LDS
 // offset 16 lane); a lane fetches the global slot that the swizzle puts
-// there (vswz of those rows is 2i).  Issued after the K loads so that
-// waiting for K does not wait for V.
+// there.  Issued after the K loads so that waiting for K does not wait for
+// V.
 template <bool STREAM>
 __device__ __forceinline__ void load_v_lds(const uint8_t* __restrict__ v_pool, size_t row0,
                                            int lane, uint8_t* page_rows) {
   const uint8_t* vp = v_pool + (row0 + (lane >> 4)) * 256;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    __builtin_amdgcn_global_load_lds(vp + 1024 * i + 16 * ((lane & 15) ^ (2 * i)),
+    __builtin_amdgcn_global_load_lds(vp + 1024 * i + 16 * ((lane & 15) ^ vswz<0>(4 * i)),
                                      (lds_void*)(page_rows + 1024 * i), 16, 0,
                                      STREAM ? kNonTemporal : 0);
 }
@@ -217,7 +232,7 @@ __device__ __forceinline__ void stage_v(const Chunk<KV>& c, uint8_t* page_rows, 
       // 128-bit LDS writes whichever lane grouping serves them.
       const int k = 8 * i + (lane >> 3);
       const bool odd = ((lane >> 2) ^ k) & 1;
-      uint8_t* dst = page_rows + voff(k, 2 * (lane & 7));
+      uint8_t* dst = page_rows + voff<KV>(k, 2 * (lane & 7));
       lds_write16(dst + (odd ? 16 : 0), odd ? o[4] : o[0], odd ? o[5] : o[1],
                   odd ? o[6] : o[2], odd ? o[7] : o[3]);
       lds_write16(dst + (odd ? 0 : 16), odd ? o[0] : o[4], odd ? o[1] : o[5],
@@ -231,16 +246,16 @@ __device__ __forceinline__ void stage_v(const Chunk<KV>& c, uint8_t* page_rows, 
     // Write w of a lane stores a rotated piece pc, so that any 8
     // consecutive lanes (two rows) write 8 distinct 16-byte slots modulo
     // 128 bytes and any 16 lanes (four rows) 16 distinct slots modulo 256
-    // bytes: no bank conflicts on the 128-bit LDS writes.
+    // bytes under the swizzle: no bank conflicts on the 128-bit LDS writes.
     const int k = lane >> 2;
-    const int rot = ((lane & 3) >> 1) + 2 * (k & 1) + ((k >> 1) & 1);
+    const int rot = ((lane & 3) >> 1) + (lane & 1);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const int pc = (w + rot) & 3;
       const uint32_t word = pc == 0 ? src[0] : (pc == 1 ? src[1] : (pc == 2 ? src[2] : src[3]));
       uint32_t o[4];
       e2m1x8_to_bf16(word, pc < 2 ? s0 : s1, o);
-      lds_write16(page_rows + voff(k, 4 * (lane & 3) + pc), o[0], o[1], o[2], o[3]);
+      lds_write16(page_rows + voff<KV>(k, 4 * (lane & 3) + pc), o[0], o[1], o[2], o[3]);
     }
   }
 }
@@ -402,20 +417,37 @@ __global__ __launch_bounds__(64 * W, 4) void sparse_attn_kernel(
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // O^T += V^T P^T, dims in blocks of 16
+    // O^T += V^T P^T, dims in blocks of 16.  The operand of lane (dim hl,
+    // group g4) is keys kappa(g4, 0..7) of its dim, the order of P^T.  A
+    // transposing read gives lane i of a 16-lane group element e of lane
+    // 4 e + i / 4, so there lane j of the group points at 4 dims
+    // (4 (j mod 4) ..) of row 4 g4 + j / 4, and the row 16 further on for
+    // the second half.
+    const int vrow = 4 * g4 + (hl >> 2);
+    const uint8_t* vrd = stage + vrow * kVRow + 8 * (hl & 3);
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      // dim 16 s + hl of rows kappa(g4, .), all with vswz = 2 g4
-      const uint8_t* col = stage + 32 * (s ^ g4) + 2 * hl;
-      uint32_t a[4];
+      bf16x8 aop;
+      if constexpr (KV == 0) {
+        // dim 16 s + hl of rows kappa(g4, .), all with vswz = 2 g4
+        const uint8_t* col = stage + 32 * (s ^ g4) + 2 * hl;
+        uint32_t a[4];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t x0 = *reinterpret_cast<const uint16_t*>(col + kappa(g4, 2 * w) * kVRow);
-        const uint32_t x1 = *reinterpret_cast<const uint16_t*>(col + kappa(g4, 2 * w + 1) * kVRow);
-        a[w] = x0 | (x1 << 16);
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t x0 = *reinterpret_cast<const uint16_t*>(col + kappa(g4, 2 * w) * kVRow);
+          const uint32_t x1 =
+              *reinterpret_cast<const uint16_t*>(col + kappa(g4, 2 * w + 1) * kVRow);
+          a[w] = x0 | (x1 << 16);
+        }
+        const u32x4 av = {a[0], a[1], a[2], a[3]};
+        aop = __builtin_bit_cast(bf16x8, av);
+      } else {
+        const uint8_t* p0 = vrd + 32 * (s ^ (vrow & 7));
+        const v4i16 k0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p0);
+        const v4i16 k1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p0 + 16 * kVRow));
+        const v8i16 kv = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+        aop = __builtin_bit_cast(bf16x8, kv);
       }
-      const u32x4 av = {a[0], a[1], a[2], a[3]};
-      const bf16x8 aop = __builtin_bit_cast(bf16x8, av);
       oacc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, phi, oacc[s], 0, 0, 0);
       oacc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, plo, oacc[s], 0, 0, 0);
     }
