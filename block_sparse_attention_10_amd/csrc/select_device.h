@@ -86,13 +86,17 @@ __device__ __forceinline__ int key_id(uint64_t k) {
 
 constexpr int kCap = 128;  // survivors of the threshold a row can rank (2 per lane)
 
-// LDS a selecting workgroup needs.  Row slot q of a pass is served by waves
-// q * parts .. q * parts + parts - 1.
+// LDS a selecting workgroup of NW waves needs (NW = 4, or 8 for one long
+// row).  Row slot q of a pass is served by waves q * parts .. q * parts +
+// parts - 1.
+template <int NW>
 struct SelectLds {
-  uint64_t survivors[4][kCap];    // keys at or above the row's threshold
-  uint64_t finalists[4 * kList];  // list path: wave w's picks at [w * K1, w * K1 + K1)
-  uint64_t bound[4];              // per wave: its K1-th best lane maximum, or 0
-  int32_t count[4];               // survivors per row slot
+  uint64_t survivors[NW == 8 ? 1 : 4][kCap];  // keys at or above the row's threshold
+  // list path, 4 waves: wave w's picks at [w * K1, w * K1 + K1) (8 waves put
+  // their picks among the survivors instead)
+  uint64_t finalists[NW == 8 ? 1 : 4 * kList];
+  uint64_t bound[NW];  // per wave: its K1-th best lane maximum, or 0
+  int32_t count[4];    // survivors per row slot
   int32_t row_sel[4][kMaxTopk];
 };
 
@@ -188,8 +192,8 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
 }
 
 // Selection (and, when page_table is given, the page table) for every row of
-// request b.  Called by all 256 threads of a 4-wave workgroup; contains
-// workgroup barriers.
+// request b.  Called by all threads of an NW-wave workgroup (NW = 8 only for
+// single-row requests); contains workgroup barriers.
 //
 // Per row: every lane takes the best key among its candidates; each wave
 // finds the K1-th best of its lane maxima (K1 = topk - 1) by counting.  That key has
@@ -200,17 +204,18 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
 // the best keys) take the list path instead: per-lane sorted lists of the
 // K1 best keys, K1 wave-max pops per wave, and a merge-rank of the waves'
 // picks.
+template <int NW>
 __device__ __forceinline__ void select_request(int b, const float* __restrict__ scores,
                                             const int32_t* __restrict__ ctx_lens,
                                             const int32_t* __restrict__ block_table,
                                             int32_t* __restrict__ selected,
                                             int32_t* __restrict__ n_selected,
                                             int32_t* __restrict__ page_table, int T, int MAXB,
-                                            int topk, SelectLds& sh) {
+                                            int topk, SelectLds<NW>& sh) {
   const int lane = lane_id();
   const int wave = wave_id();
-  const int parts = T >= 4 ? 1 : (T == 1 ? 4 : (T == 2 ? 2 : 1));
-  const int rows_per_pass = 4 / parts;
+  const int parts = NW == 8 ? 8 : (T >= 4 ? 1 : (T == 1 ? 4 : (T == 2 ? 2 : 1)));
+  const int rows_per_pass = NW / parts;
   const int K1 = topk - 1;
   const int stride = parts * kWave;
   const int part = wave % parts;
@@ -244,19 +249,20 @@ __device__ __forceinline__ void select_request(int b, const float* __restrict__ 
     const bool work = active && !take_all && K1 > 0;
     if (part == 0 && lane == 0) sh.count[slot] = 0;
 
-    // lane maxima; the orderable scores of the first two batches stay in
-    // registers
+    // lane maxima; the orderable scores of the first two batches (one with
+    // 8 waves, which keeps the registers below 256) stay in registers
+    constexpr bool kTwo = NW == 4;
     float sv2[kBatch];
     uint32_t ok0[kBatch], ok1[kBatch];
     const int c1 = cfirst + kBatch * stride;
-    const int c2 = c1 + kBatch * stride;
+    const int c2 = kTwo ? c1 + kBatch * stride : c1;  // first candidate re-read
     const int nw0 = wave_slots(cfirst, lane, stride, local);
     const int nw1 = wave_slots(c1, lane, stride, local);
     uint64_t lmax = 0;  // 0 ranks below every real key
     if (work) {
-      if (nw1 > 0) load_batch(sv2, srow, c1, stride, local);
+      if (kTwo && nw1 > 0) load_batch(sv2, srow, c1, stride, local);
       key_batch(ok0, sv, lmax, cfirst, stride, local, nw0);
-      if (nw1 > 0) key_batch(ok1, sv2, lmax, c1, stride, local, nw1);
+      if (kTwo && nw1 > 0) key_batch(ok1, sv2, lmax, c1, stride, local, nw1);
       for (int c0 = c2; c0 - lane < local; c0 += kBatch * stride) {  // wave-uniform
         float sx[kBatch];
         uint32_t okx[kBatch];
@@ -284,8 +290,8 @@ __device__ __forceinline__ void select_request(int b, const float* __restrict__ 
       bound = x > bound ? x : bound;
     }
     if (work) {
-      int mine = pass_keys<false>(ok0, cfirst, stride, bound, nw0, nullptr, 0) +
-                 pass_keys<false>(ok1, c1, stride, bound, nw1, nullptr, 0);
+      int mine = pass_keys<false>(ok0, cfirst, stride, bound, nw0, nullptr, 0);
+      if (kTwo) mine += pass_keys<false>(ok1, c1, stride, bound, nw1, nullptr, 0);
       for (int c0 = c2; c0 - lane < local; c0 += kBatch * stride) {  // wave-uniform
         float sx[kBatch];
         uint32_t okx[kBatch];
@@ -312,7 +318,7 @@ __device__ __forceinline__ void select_request(int b, const float* __restrict__ 
         const int n0 = pass_keys<true>(ok0, cfirst, stride, bound, nw0, out, room);
         out += n0;
         room -= n0;
-        if (room > 0) {
+        if (kTwo && room > 0) {
           const int n1 = pass_keys<true>(ok1, c1, stride, bound, nw1, out, room);
           out += n1;
           room -= n1;
@@ -344,13 +350,14 @@ __device__ __forceinline__ void select_request(int b, const float* __restrict__ 
         insert_batch(list, sx, c0, stride, local);
       }
       // this wave's K1 best keys, best first; 0 once its lists run dry
+      uint64_t* picks = (NW == 8 ? sh.survivors[slot] : sh.finalists) + wave * K1;
       for (int k = 0; k < K1; ++k) {
         const uint64_t best = wave_max_u64(list[0]);
         if (best == 0) {  // wave-uniform
-          for (int e = lane; e < K1 - k; e += kWave) sh.finalists[wave * K1 + k + e] = 0;
+          for (int e = lane; e < K1 - k; e += kWave) picks[k + e] = 0;
           break;
         }
-        if (lane == 0) sh.finalists[wave * K1 + k] = best;
+        if (lane == 0) picks[k] = best;
         if (list[0] == best) {
 #pragma unroll
           for (int j = 0; j < kList - 1; ++j) list[j] = list[j + 1];
@@ -369,16 +376,23 @@ __device__ __forceinline__ void select_request(int b, const float* __restrict__ 
         if (lane == 0) row_sel[wave][0] = local;
         n = 1;
       } else {
-        if (!list_path) {
+        // the K1 best keys go to row_sel[wave][rank] (keys are unique, so
+        // ranks 0 .. K1 - 1 each have exactly one owner)
+        if (!list_path || NW == 8) {
+          // rank by counting among the survivors, or (8 waves, list path)
+          // among the waves' picks, which may hold zeros
+          const int me = list_path ? parts * K1 : m;
           uint64_t* sv_ = sh.survivors[slot];
-          const uint64_t e0 = lane < m ? sv_[lane] : 0;
-          const uint64_t e1 = lane + kWave < m ? sv_[lane + kWave] : 0;
-          if (lane < 8 && m + lane < kCap) sv_[m + lane] = 0;
+          const uint64_t e0 = lane < me ? sv_[lane] : 0;
+          const uint64_t e1 = lane + kWave < me ? sv_[lane + kWave] : 0;
+          // zeros up to a multiple of 8 (they rank below every key), then
+          // 8 keys per step
+          if (lane < 8 && me + lane < kCap) sv_[me + lane] = 0;
           __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
           __builtin_amdgcn_wave_barrier();
           __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
           int r0 = 0, r1 = 0;
-          for (int j = 0; j < m; j += 8) {
+          for (int j = 0; j < me; j += 8) {
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
               const uint64_t x = sv_[j + q];
@@ -386,15 +400,20 @@ __device__ __forceinline__ void select_request(int b, const float* __restrict__ 
               r1 += x > e1 ? 1 : 0;
             }
           }
-          if (lane < m && r0 < K1) row_sel[wave][r0] = key_id(e0);
-          if (lane + kWave < m && r1 < K1) row_sel[wave][r1] = key_id(e1);
+          if (lane < me && (NW == 4 || e0 != 0) && r0 < K1) row_sel[wave][r0] = key_id(e0);
+          if (lane + kWave < me && (NW == 4 || e1 != 0) && r1 < K1)
+            row_sel[wave][r1] = key_id(e1);
         } else {
+          // merge-rank of the waves' picks: each wave's list is sorted best
+          // first (zeros last) and keys are unique, so a pick's rank is its
+          // index plus, per other list, the count of better keys there (a
+          // binary search)
           const int mf = parts * K1;
           const uint64_t* fin = sh.finalists + wave * K1;
           const uint64_t mine = lane < mf ? fin[lane] : 0;
           const int own = lane < mf ? lane / K1 : 0;
           int rank = lane - own * K1;
-          for (int w = 0; w < parts; ++w) {
+          for (int w = 0; w < parts; ++w) {  // wave-uniform
             if (w == own) continue;
             const uint64_t* list = fin + w * K1;
             int cnt = 0;
@@ -405,6 +424,7 @@ __device__ __forceinline__ void select_request(int b, const float* __restrict__ 
           }
           if (lane < mf && rank < K1 && mine != 0) row_sel[wave][rank] = key_id(mine);
         }
+        // order the K1 winners by id: lane k places the k-th ranked one
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");

@@ -21,14 +21,15 @@
 namespace msa {
 namespace {
 
-__global__ __launch_bounds__(256) void select_kernel(
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void select_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ ctx_lens,
     const int32_t* __restrict__ block_table, int32_t* __restrict__ selected,
     int32_t* __restrict__ n_selected, int32_t* __restrict__ page_table, int T, int MAXB,
     int topk) {
-  __shared__ SelectLds sh;
-  select_request(blockIdx.x, scores, ctx_lens, block_table, selected, n_selected, page_table,
-                 T, MAXB, topk, sh);
+  __shared__ SelectLds<NW> sh;
+  select_request<NW>(blockIdx.x, scores, ctx_lens, block_table, selected, n_selected,
+                     page_table, T, MAXB, topk, sh);
 }
 
 __global__ __launch_bounds__(256) void page_table_kernel(const int32_t* __restrict__ selected,
@@ -48,14 +49,25 @@ __global__ __launch_bounds__(256) void page_table_kernel(const int32_t* __restri
 
 }  // namespace
 
+// Rows of at least this many blocks (single-row requests) select with 8
+// waves per request.
+constexpr int kLongRowBlocks = 2048;
+
 hipError_t launch_select(const Dims& d, const float* scores, const int32_t* ctx_lens,
                          const int32_t* block_table, int32_t* selected, int32_t* n_selected,
                          int32_t* page_table, hipStream_t s, std::string* note) {
-  hipLaunchKernelGGL(select_kernel, dim3(d.B), dim3(256), 0, s, scores, ctx_lens, block_table,
-                     selected, n_selected, page_table, d.T, d.MAXB, d.topk);
+  // single-row requests with long rows: 8 waves, so that each lane holds
+  // half as many candidates
+  const int nw = d.T == 1 && d.MAXB >= kLongRowBlocks ? 8 : 4;
+  if (nw == 8)
+    hipLaunchKernelGGL((select_kernel<8>), dim3(d.B), dim3(512), 0, s, scores, ctx_lens,
+                       block_table, selected, n_selected, page_table, d.T, d.MAXB, d.topk);
+  else
+    hipLaunchKernelGGL((select_kernel<4>), dim3(d.B), dim3(256), 0, s, scores, ctx_lens,
+                       block_table, selected, n_selected, page_table, d.T, d.MAXB, d.topk);
   if (note)
-    *note += std::string("select_topk[grid=") + std::to_string(d.B) + "x256" +
-             (page_table ? ",+pages]" : "]");
+    *note += std::string("select_topk[grid=") + std::to_string(d.B) + "x" +
+             std::to_string(64 * nw) + (page_table ? ",+pages]" : "]");
   return hipGetLastError();
 }
 

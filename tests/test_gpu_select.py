@@ -20,10 +20,17 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def lane_of(c, T):
+def parts_for(T, MAXB):
+    """Waves per row: 8 for single-row requests of 2048 blocks or more, else 4
+    / T (1 from 3 rows on), as the selection kernel splits a row."""
+    if T == 1:
+        return 8 if MAXB >= 2048 else 4
+    return 2 if T == 2 else 1
+
+
+def lane_of(c, T, MAXB):
     """(wave part, lane) that reads candidate c for T rows per request."""
-    parts = 1 if T >= 3 else (4 if T == 1 else 2)
-    stride = parts * 64
+    stride = parts_for(T, MAXB) * 64
     return (c % stride) // 64, c % 64
 
 
@@ -48,7 +55,7 @@ def make_scores(pattern, R, MAXB, T, rng):
         # lanes 0..14 of the first wave hold every key above the rest, each
         # lane's keys above the previous lane's: the wave bound is lane 0's
         # maximum and almost all of lanes 1..14's keys reach it
-        part, lane = lane_of(c, T)
+        part, lane = lane_of(c, T, MAXB)
         s = rng.standard_normal((R, MAXB))
         hot = (part == 0) & (lane < 15)
         s[:, hot] = 1000.0 + 100.0 * lane[hot] + (c[hot] // 256) % 32
@@ -104,22 +111,26 @@ def test_selection_matches_oracle_on_crafted_scores(case, pattern):
 
 
 def test_lane_clustered_rows_take_the_list_path_and_iid_rows_do_not():
-    # The survivors of the threshold for one long row: the clustered layout
-    # leaves far more than a row can rank by counting (128), iid scores a few
-    # dozen.  Counted here on the host from the same rule the kernel applies.
-    T, L = 1, 1_100_000
-    MAXB = -(-L // 128)
-    local = (L - 1) >> 7
+    # The survivors of the threshold for one long single-row request (8
+    # waves) and a two-row request (2 of the 4 waves per row): the clustered
+    # layout leaves far more than a row
+    # can rank by counting (128), iid scores a few dozen.  Counted here on
+    # the host from the same rule the kernel applies.
     rng = np.random.default_rng(3)
-    for pattern, many in (("lane_clustered", True), ("iid", False)):
+    for (T, L), pattern, many in (((1, 1_100_000), "lane_clustered", True),
+                                  ((1, 1_100_000), "iid", False),
+                                  ((2, 600_000), "lane_clustered", True),
+                                  ((2, 600_000), "iid", False)):
+        MAXB = -(-L // 128)
+        local = (L - 1) >> 7
         s = make_scores(pattern, 1, MAXB, T, rng)[0]
         keys = [(float(s[c]), -c) for c in range(local)]
         lanes = {}
         for c in range(local):
-            part, lane = lane_of(c, T)
+            part, lane = lane_of(c, T, MAXB)
             lanes.setdefault((part, lane), []).append(keys[c])
         bound = None
-        for part in range(4):
+        for part in range(parts_for(T, MAXB)):
             maxima = sorted((max(v) for (pt, _), v in lanes.items() if pt == part), reverse=True)
             if len(maxima) >= 15:
                 b = maxima[14]
