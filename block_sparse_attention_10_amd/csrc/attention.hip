@@ -530,20 +530,34 @@ __global__ __launch_bounds__(64 * W, 4) void sparse_attn_kernel(
 }
 
 // out[rh][d] = sum_s 2^(m_s - M) O_s[d] / sum_s 2^(m_s - M) l_s
+// Splits per row never exceed kMaxSplits (at most 64 chunks of 32 keys per
+// row, at least 8 per split); every split's (m, l) and partial row load in
+// one round trip, then combine in split order.
+constexpr int kMaxSplits = 8;
+
 __global__ __launch_bounds__(128) void lse_merge_kernel(const float* __restrict__ part_o,
                                                         const float* __restrict__ part_ml,
                                                         float* __restrict__ out, int S) {
   const size_t rh = blockIdx.x;
   const int d = threadIdx.x;
   const float* ml = part_ml + rh * S * 2;
+  float ms[kMaxSplits], ls[kMaxSplits], os[kMaxSplits];
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) {
+    ms[s] = s < S ? ml[2 * s] : neg_inf();
+    ls[s] = s < S ? ml[2 * s + 1] : 0.f;
+    os[s] = s < S ? part_o[(rh * S + s) * kD + d] : 0.f;
+  }
   float M = neg_inf();
-  for (int s = 0; s < S; ++s) M = fmaxf(M, ml[2 * s]);
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) M = fmaxf(M, ms[s]);
   float O = 0.f, Ls = 0.f;
-  for (int s = 0; s < S; ++s) {
-    const float ms = ml[2 * s];
-    const float f = ms == neg_inf() ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-    O += f * part_o[(rh * S + s) * kD + d];
-    Ls += f * ml[2 * s + 1];
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) {
+    if (s >= S) break;
+    const float f = ms[s] == neg_inf() ? 0.f : __builtin_amdgcn_exp2f(ms[s] - M);
+    O += f * os[s];
+    Ls += f * ls[s];
   }
   out[rh * kD + d] = Ls > 0.f ? O / Ls : 0.f;
 }
@@ -649,6 +663,7 @@ hipError_t launch_sparse_attention(const Dims& d, const void* q, const void* k_p
              std::to_string(attention_workgroups(d, sp)) + "x" + std::to_string(64 * sp.waves) +
              ",splits=" + std::to_string(sp.splits) + "]";
   if (sp.splits > 1) {
+    if (sp.splits > kMaxSplits) return hipErrorInvalidValue;
     const unsigned rows = (unsigned)((long)d.R() * d.Hq);
     hipLaunchKernelGGL(lse_merge_kernel, dim3(rows), dim3(kD), 0, s, part_o, part_ml, out,
                        sp.splits);
