@@ -86,7 +86,8 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        path = _LIB if os.path.exists(_LIB) else build()
+        # MSA_ORACLE_LIB: another build of the same source (the sanitizer test)
+        path = os.environ.get("MSA_ORACLE_LIB") or (_LIB if os.path.exists(_LIB) else build())
         L = ctypes.CDLL(path)
         vp = ctypes.c_void_p
         pp = ctypes.POINTER(_Problem)
