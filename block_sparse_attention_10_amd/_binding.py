@@ -13,7 +13,9 @@ from typing import Optional
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmsa.so")
+# MSA_LIBRARY: another build of the same sources (the host-sanitizer test)
+_LIB_PATH = os.environ.get("MSA_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libmsa.so")
 
 MSA_OK = 0
 MSA_ERR_INVALID_ARG = -1
