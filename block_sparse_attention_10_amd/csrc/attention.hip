@@ -155,8 +155,9 @@ __device__ __forceinline__ void load_page(Chunk<KV>& c, const uint8_t* __restric
 // bf16 V of one page straight from HBM into its LDS rows, no registers
 // involved.  Load i fills rows 4i..4i+3 (1 KB, 16 bytes per lane at LDS
 // offset 16 lane); a lane fetches the global slot that the swizzle puts
-// there.  Issued after the K loads so that waiting for K does not wait for
-// V.
+// there.  The compiler issues these after the chunk's S^T MFMAs, i.e. once
+// K has arrived; issuing them ahead of the MFMAs (K and V in flight
+// together) measured slower on MI355X.
 template <bool STREAM>
 __device__ __forceinline__ void load_v_lds(const uint8_t* __restrict__ v_pool, size_t row0,
                                            int lane, uint8_t* page_rows) {
