@@ -58,6 +58,10 @@ int check_problem(const msa_problem* p, Dims* d) {
   if (p->kv_dtype < MSA_DTYPE_BF16 || p->kv_dtype > MSA_DTYPE_NVFP4) return MSA_ERR_UNSUPPORTED;
   if (p->idx_k_dtype < MSA_DTYPE_BF16 || p->idx_k_dtype > MSA_DTYPE_NVFP4)
     return MSA_ERR_UNSUPPORTED;
+  // An int32 context spans at most 2^24 blocks (block offsets c * 128 stay
+  // in int32), and page ids phys * 8 + j must fit int32.
+  if (p->max_blocks_per_seq > (1 << 24) || p->num_phys_blocks > (1 << 28))
+    return MSA_ERR_UNSUPPORTED;
   // grid limits: one wave per (request, block) in the scan
   if ((long)p->batch * p->max_blocks_per_seq > (1L << 30) ||
       (long)p->batch * p->decode_query_len * p->num_q_heads > (1L << 30))

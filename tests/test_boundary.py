@@ -73,6 +73,11 @@ def good(**kw):
     (dict(decode_query_len=17), msa.MSA_ERR_UNSUPPORTED),
     (dict(num_q_heads=32, num_kv_heads=1), msa.MSA_ERR_UNSUPPORTED),
     (dict(num_idx_heads=17), msa.MSA_ERR_UNSUPPORTED),
+    (dict(max_blocks_per_seq=(1 << 24) + 1), msa.MSA_ERR_UNSUPPORTED),
+    (dict(num_phys_blocks=(1 << 28) + 1), msa.MSA_ERR_UNSUPPORTED),
+    (dict(batch=65, max_blocks_per_seq=1 << 24), msa.MSA_ERR_UNSUPPORTED),
+    (dict(batch=1 << 19, num_q_heads=256, num_kv_heads=16, decode_query_len=16),
+     msa.MSA_ERR_UNSUPPORTED),
 ])
 def test_bad_problems_are_rejected(kw, code):
     p = good(**kw)
@@ -81,6 +86,14 @@ def test_bad_problems_are_rejected(kw, code):
     t = msa.Tensors()
     assert L.msa_index_score(ctypes.byref(p), ctypes.byref(t), None, None) == code
     assert L.msa_decode(ctypes.byref(p), ctypes.byref(t), None, None, None, None, 0, None) == code
+
+
+def test_largest_supported_sizes_are_accepted():
+    # 2^24 blocks cover the longest int32 context; 2^28 physical blocks keep
+    # page ids in int32
+    for kw in (dict(batch=1, max_blocks_per_seq=1 << 24), dict(num_phys_blocks=1 << 28),
+               dict(batch=64, max_blocks_per_seq=1 << 24)):
+        assert msa.msa_workspace_bytes(good(**kw)) > 0, kw
 
 
 def test_struct_size_is_checked():
