@@ -62,9 +62,14 @@ int check_problem(const msa_problem* p, Dims* d) {
   // in int32), and page ids phys * 8 + j must fit int32.
   if (p->max_blocks_per_seq > (1 << 24) || p->num_phys_blocks > (1 << 28))
     return MSA_ERR_UNSUPPORTED;
-  // grid limits: one wave per (request, block) in the scan
-  if ((long)p->batch * p->max_blocks_per_seq > (1L << 30) ||
-      (long)p->batch * p->decode_query_len * p->num_q_heads > (1L << 30))
+  // Grid limits (a launch holds fewer than 2^32 work-items): the scan runs
+  // one 64-lane wave per (request, block); attention, merge and the write
+  // path (one wave per row and K, V or index head) stay below 2^31
+  // work-items with at most 2^22 (row, query head) and (row, index head)
+  // pairs.
+  const long rows = (long)p->batch * p->decode_query_len;
+  if ((long)p->batch * p->max_blocks_per_seq > (1L << 25) ||
+      rows * p->num_q_heads > (1L << 22) || rows * p->num_idx_heads > (1L << 22))
     return MSA_ERR_UNSUPPORTED;
   d->B = p->batch;
   d->T = p->decode_query_len;

@@ -64,8 +64,9 @@
  *  - Supported shape: head_dim 128, idx_dim 64, block_size 128, page_size 16,
  *    local_blocks 1, 1 <= topk <= 16, 1 <= Hq/Hkv <= 16, 1 <= T <= 16,
  *    1 <= Hidx <= 16; MAXB <= 2^24 (the blocks of the longest int32
- *    context), NB <= 2^28 (page ids fit int32), B * MAXB <= 2^30 and
- *    B * T * Hq <= 2^30.  Anything else returns MSA_ERR_UNSUPPORTED.
+ *    context), NB <= 2^28 (page ids fit int32), B * MAXB <= 2^25,
+ *    B * T * Hq <= 2^22 and B * T * Hidx <= 2^22 (every launch below 2^32
+ *    work-items).  Anything else returns MSA_ERR_UNSUPPORTED.
  *  - Return codes: MSA_OK when every launch was enqueued; MSA_ERR_INVALID_ARG
  *    for a NULL pointer, a misaligned pointer or an inconsistent dimension;
  *    MSA_ERR_UNSUPPORTED for a dtype or shape outside the list above;

@@ -75,8 +75,10 @@ def good(**kw):
     (dict(num_idx_heads=17), msa.MSA_ERR_UNSUPPORTED),
     (dict(max_blocks_per_seq=(1 << 24) + 1), msa.MSA_ERR_UNSUPPORTED),
     (dict(num_phys_blocks=(1 << 28) + 1), msa.MSA_ERR_UNSUPPORTED),
-    (dict(batch=65, max_blocks_per_seq=1 << 24), msa.MSA_ERR_UNSUPPORTED),
-    (dict(batch=1 << 19, num_q_heads=256, num_kv_heads=16, decode_query_len=16),
+    (dict(batch=3, max_blocks_per_seq=1 << 24), msa.MSA_ERR_UNSUPPORTED),
+    (dict(batch=(1 << 18) + 1, num_idx_heads=16, decode_query_len=1, num_q_heads=1,
+          max_blocks_per_seq=1), msa.MSA_ERR_UNSUPPORTED),
+    (dict(batch=(1 << 14) + 1, num_q_heads=16, num_kv_heads=1, decode_query_len=16),
      msa.MSA_ERR_UNSUPPORTED),
 ])
 def test_bad_problems_are_rejected(kw, code):
@@ -92,7 +94,9 @@ def test_largest_supported_sizes_are_accepted():
     # 2^24 blocks cover the longest int32 context; 2^28 physical blocks keep
     # page ids in int32
     for kw in (dict(batch=1, max_blocks_per_seq=1 << 24), dict(num_phys_blocks=1 << 28),
-               dict(batch=64, max_blocks_per_seq=1 << 24)):
+               dict(batch=2, max_blocks_per_seq=1 << 24),
+               dict(batch=1 << 18, num_idx_heads=16, num_q_heads=1, max_blocks_per_seq=1),
+               dict(batch=1 << 14, num_q_heads=16, num_kv_heads=1, decode_query_len=16)):
         assert msa.msa_workspace_bytes(good(**kw)) > 0, kw
 
 
