@@ -197,8 +197,8 @@ def main():
         return
 
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported by this build "
-              "(the path shards by request or by context across GPUs, see the design notes).",
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (across GPUs the "
+              "path would shard by request, or by context with two small exchanges).",
               file=sys.stderr)
         sys.exit(2)
 
