@@ -13,8 +13,8 @@
 //  * A workgroup of 4 or 8 waves owns one (row, KV head, split).  Each wave
 //    walks chunks of 32 keys (two 16-token pages) of the row's blocks; when
 //    a workgroup holds the whole row it writes the output itself.  Draft
-//    rows of one request run on one XCD, so blocks they share are read from
-//    HBM once and from L2 after.
+//    rows of one request run on one XCD, so blocks they share can be served
+//    from its L2.
 //  * QK^T on MFMA v_mfma_f32_16x16x32_bf16 with keys as the M dimension and
 //    the query heads of the KV head as N (one tile of 16): S^T = K Q^T; keys
 //    past the row's position are masked.  K rows go straight from HBM into
@@ -109,20 +109,20 @@ __device__ __forceinline__ int kdim(int g, int kk) {
   else return 32 * g + 8 * kk;                                            // whole 64 B row
 }
 
-// KV pages of one call are read once when every workgroup owns distinct
-// pages (non-temporal hint), and kept cacheable when row groups of a
-// request share them.
-template <bool STREAM>
-__device__ __forceinline__ u32x4 ld16(const uint8_t* p) {
-  if constexpr (STREAM) return ldg128_stream(p);
-  else return ldg128(p);
-}
+// Every KV load carries the non-temporal hint, also where the draft rows of
+// a request share pages.  Measured on MI355X (fp8 spec-verify layer, 128
+// requests x 4 rows): after a 1 GiB cache flush, the state of a layer's KV
+// in a decode step over many layers, a step takes 91.5 us with the hint
+// against 116.5 us with cached loads; only when the same layer repeats back
+// to back, its ~220 MB of KV then staying in the 256 MB last-level cache,
+// do cached loads win (64 vs 75 us).
+__device__ __forceinline__ u32x4 ld16(const uint8_t* p) { return ldg128_stream(p); }
 
 // Register loads of one 16-token page.  K: lane (key m = lane % 16, group
 // g) holds the slices kdim(g, .) of key m.  fp8 / 4-bit V: each load
 // instruction covers a contiguous run (1 KB for fp8, the whole page for
 // 4-bit), widened to bf16 by stage_v.  bf16 V takes load_v_lds instead.
-template <int KV, bool STREAM>
+template <int KV>
 __device__ __forceinline__ void load_page(Chunk<KV>& c, const uint8_t* __restrict__ k_pool,
                                           const uint8_t* __restrict__ v_pool,
                                           const void* __restrict__ k_scale,
@@ -132,19 +132,19 @@ __device__ __forceinline__ void load_page(Chunk<KV>& c, const uint8_t* __restric
   if constexpr (KV == 0) {
     const uint8_t* kp = k_pool + (row0 + m) * 256 + 16 * g;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) c.k[i] = ld16<STREAM>(kp + 64 * i);
+    for (int i = 0; i < 4; ++i) c.k[i] = ld16(kp + 64 * i);
   } else if constexpr (KV == 1) {
     const uint8_t* kp = k_pool + (row0 + m) * 128 + 16 * g;
     const uint8_t* vp = v_pool + row0 * 128 + 16 * lane;
-    c.k[0] = ld16<STREAM>(kp);
-    c.k[1] = ld16<STREAM>(kp + 64);
-    c.v[0] = ld16<STREAM>(vp);
-    c.v[1] = ld16<STREAM>(vp + 1024);
+    c.k[0] = ld16(kp);
+    c.k[1] = ld16(kp + 64);
+    c.v[0] = ld16(vp);
+    c.v[1] = ld16(vp + 1024);
     c.kscale = *reinterpret_cast<const f32x4*>(static_cast<const float*>(k_scale) + row0 + 4 * g);
     c.vscale = *reinterpret_cast<const f32x4*>(static_cast<const float*>(v_scale) + row0 + 4 * g);
   } else {
-    c.k[0] = ld16<STREAM>(k_pool + (row0 + m) * 64 + 16 * g);
-    c.v[0] = ld16<STREAM>(v_pool + row0 * 64 + 16 * lane);
+    c.k[0] = ld16(k_pool + (row0 + m) * 64 + 16 * g);
+    c.v[0] = ld16(v_pool + row0 * 64 + 16 * lane);
     c.ks = *reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(k_scale) +
                                               (row0 + m) * 8 + 2 * g);
     c.vs = *reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(v_scale) +
@@ -158,7 +158,6 @@ __device__ __forceinline__ void load_page(Chunk<KV>& c, const uint8_t* __restric
 // there.  The compiler issues these after the chunk's S^T MFMAs, i.e. once
 // K has arrived; issuing them ahead of the MFMAs (K and V in flight
 // together) measured slower on MI355X.
-template <bool STREAM>
 __device__ __forceinline__ void load_v_lds(const uint8_t* __restrict__ v_pool, size_t row0,
                                            int lane, uint8_t* page_rows) {
   const uint8_t* vp = v_pool + (row0 + (lane >> 4)) * 256;
@@ -166,7 +165,7 @@ __device__ __forceinline__ void load_v_lds(const uint8_t* __restrict__ v_pool, s
   for (int i = 0; i < 4; ++i)
     __builtin_amdgcn_global_load_lds(vp + 1024 * i + 16 * ((lane & 15) ^ vswz<0>(4 * i)),
                                      (lds_void*)(page_rows + 1024 * i), 16, 0,
-                                     STREAM ? kNonTemporal : 0);
+                                     kNonTemporal);
 }
 
 // Four packed bf16 pairs from 8 e2m1 codes (one dword) with scale `s`.
@@ -266,7 +265,7 @@ __device__ __forceinline__ void stage_v(const Chunk<KV>& c, uint8_t* page_rows, 
 // lists its blocks, local block last.  Every wave walks chunks of 32 keys
 // (two 16-token pages) of the row's blocks, S apart between the splits and
 // S W apart between the waves of a split.
-template <int KV, int W, bool STREAM>
+template <int KV, int W>
 __global__ __launch_bounds__(64 * W, 4) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ k_pool,
     const uint8_t* __restrict__ v_pool, const void* __restrict__ k_scale,
@@ -344,7 +343,7 @@ __global__ __launch_bounds__(64 * W, 4) void sparse_attn_kernel(
     const size_t row0 = ((size_t)phys * Hkv + g) * 128 + (size_t)pg0 * 16;
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-      load_page<KV, STREAM>(ch[j], k_pool, v_pool, k_scale, v_scale, row0 + 16 * j, lane);
+      load_page<KV>(ch[j], k_pool, v_pool, k_scale, v_scale, row0 + 16 * j, lane);
     return row0;
   };
   // the online-softmax update with chunk ci
@@ -355,7 +354,7 @@ __global__ __launch_bounds__(64 * W, 4) void sparse_attn_kernel(
     if constexpr (KV == 0) {
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        load_v_lds<STREAM>(v_pool, row0 + 16 * j, lane, stage + 16 * j * kVRow);
+        load_v_lds(v_pool, row0 + 16 * j, lane, stage + 16 * j * kVRow);
     } else {
 #pragma unroll
       for (int j = 0; j < 2; ++j) stage_v<KV>(ch[j], stage + 16 * j * kVRow, lane);
@@ -590,12 +589,12 @@ long attention_workgroups(const Dims& d, const SplitPlan& sp) {
   return reqs * d.T * d.Hkv * sp.splits;
 }
 
-template <int KV, int W, bool STREAM>
+template <int KV, int W>
 hipError_t launch_kvw(const Dims& d, const SplitPlan& sp, const void* q, const void* k_pool,
                       const void* v_pool, const void* k_scale, const void* v_scale,
                       const int32_t* page_table, const int32_t* ctx_lens, float* part_o,
                       float* part_ml, float* out, hipStream_t s) {
-  hipLaunchKernelGGL((sparse_attn_kernel<KV, W, STREAM>),
+  hipLaunchKernelGGL((sparse_attn_kernel<KV, W>),
                      dim3((unsigned)attention_workgroups(d, sp)), dim3(64 * W), 0, s,
                      static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(k_pool),
                      static_cast<const uint8_t*>(v_pool), k_scale, v_scale, page_table,
@@ -609,18 +608,11 @@ hipError_t launch_kv(const Dims& d, const SplitPlan& sp, const void* q, const vo
                      const void* v_pool, const void* k_scale, const void* v_scale,
                      const int32_t* page_table, const int32_t* ctx_lens, float* part_o,
                      float* part_ml, float* out, hipStream_t s) {
-#define MSA_ATTN(WV, ST)                                                                  \
-  return launch_kvw<KV, WV, ST>(d, sp, q, k_pool, v_pool, k_scale, v_scale, page_table, \
-                                ctx_lens, part_o, part_ml, out, s)
-  // One row per request: every page is read once, with the non-temporal
-  // hint.  Several draft rows: cached loads, so that rows sharing a block
-  // meet in L2.
-  if (d.T == 1) {
-    if (sp.waves == 8) MSA_ATTN(8, true);
-    MSA_ATTN(4, true);
-  }
-  if (sp.waves == 8) MSA_ATTN(8, false);
-  MSA_ATTN(4, false);
+#define MSA_ATTN(WV)                                                                      \
+  return launch_kvw<KV, WV>(d, sp, q, k_pool, v_pool, k_scale, v_scale, page_table, ctx_lens, \
+                            part_o, part_ml, out, s)
+  if (sp.waves == 8) MSA_ATTN(8);
+  MSA_ATTN(4);
 #undef MSA_ATTN
 }
 
