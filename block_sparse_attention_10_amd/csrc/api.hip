@@ -254,15 +254,21 @@ int msa_decode(const msa_problem* p, const msa_tensors* t, int32_t* selected,
                                         t->block_table, t->ctx_lens, scores, s, &note))))
     return e;
   note += " ";
-  if ((e = hip_status(launch_select(d, scores, t->ctx_lens, t->block_table, sel, nsel, pt, s,
-                                    &note))))
-    return e;
-  note += " ";
+  // Single-row requests select inside the attention launch (one launch
+  // fewer on the dependent chain); the rest select in a launch of their own.
+  const bool fuse = fused_select_eligible(d);
+  const SelectArgs fused{scores, t->block_table, selected, selected ? nsel : nullptr, page_table};
+  if (!fuse) {
+    if ((e = hip_status(launch_select(d, scores, t->ctx_lens, t->block_table, sel, nsel, pt, s,
+                                      &note))))
+      return e;
+    note += " ";
+  }
   if ((e = hip_status(launch_sparse_attention(d, t->q, t->k_pool, t->v_pool, t->k_scale,
                                               t->v_scale, pt, t->ctx_lens,
                                               reinterpret_cast<float*>(ws + w.part_o),
                                               reinterpret_cast<float*>(ws + w.part_ml), out, s,
-                                              &note))))
+                                              &note, fuse ? &fused : nullptr))))
     return e;
   g_last_dispatch = note;
   return MSA_OK;

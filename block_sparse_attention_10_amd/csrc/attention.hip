@@ -33,6 +33,10 @@
 //  * fp8 K/V: e4m3 -> bf16 is exact; the per-token K scale multiplies the
 //    logit, the V scale multiplies P.  4-bit K/V: e2m1 x e4m3 -> bf16 is
 //    exact (at most 6 significant bits) and happens in registers.
+//  * Inside msa_decode, single-row requests select in this launch: every
+//    workgroup of a row runs the selection (select_device.h) on the row's
+//    block scores first and keeps the page ids in LDS, which saves the
+//    selection launch on the dependent chain.
 //  * Split partials (m, l, unnormalised O) combine inside the workgroup in
 //    LDS; when a row is split over several workgroups a small merge kernel
 //    applies the log-sum-exp rule.  (Merging in the last workgroup to finish
@@ -40,6 +44,7 @@
 //    workgroup on a write-through store and a returning atomic.)
 #include "msa_device.h"
 #include "msa_internal.h"
+#include "select_device.h"
 
 #include <math.h>
 
@@ -264,15 +269,20 @@ __device__ __forceinline__ void stage_v(const Chunk<KV>& c, uint8_t* page_rows, 
 // of KV head g are the MFMA columns (zero past G), the row's page table
 // lists its blocks, local block last.  Every wave walks chunks of 32 keys
 // (two 16-token pages) of the row's blocks, S apart between the splits and
-// S W apart between the waves of a split.
-template <int KV, int W>
-__global__ __launch_bounds__(64 * W, 4) void sparse_attn_kernel(
+// S W apart between the waves of a split.  SEL (single-row requests, 8
+// waves): the workgroup first selects its row's blocks from the block scores
+// (the selection kernel's code, page ids into LDS) instead of reading a page
+// table; its registers then allow two waves per SIMD, which is all that one
+// workgroup per CU needs.
+template <int KV, int W, bool SEL>
+__global__ __launch_bounds__(64 * W, SEL ? 2 : 4) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ k_pool,
     const uint8_t* __restrict__ v_pool, const void* __restrict__ k_scale,
     const void* __restrict__ v_scale, const int32_t* __restrict__ page_table,
     const int32_t* __restrict__ ctx_lens, float* __restrict__ part_o,
     float* __restrict__ part_ml, float* __restrict__ out, int B, int T, int Hq, int Hkv, int PT,
-    int S, int max_block, float scale_log2) {
+    int S, int max_block, float scale_log2, SelectArgs sa, int MAXB) {
+  static_assert(!SEL || W == 8, "the fused selection runs on 8 waves");
   __shared__ __attribute__((aligned(16))) uint8_t smem[W * kWaveLds];
 
   const int lane = lane_id();
@@ -314,9 +324,22 @@ __global__ __launch_bounds__(64 * W, 4) void sparse_attn_kernel(
   }
 
   // the row's page table stays in registers: slot k's first page in lane 8k
-  const int32_t* prow = page_table + (size_t)r * PT;
-  const int pt_lo = lane < PT ? prow[lane] : -1;
-  const int pt_hi = lane + kWave < PT ? prow[lane + kWave] : -1;
+  int pt_lo, pt_hi;
+  if constexpr (SEL) {
+    // every workgroup of the row selects (T = 1); one of them exports
+    __shared__ SelectLds<8> ssh;
+    __shared__ int32_t prow_lds[kMaxTopk * 8];
+    const bool exporter = g == 0 && split == 0;
+    select_request<8>(b, sa.scores, ctx_lens, sa.block_table, exporter ? sa.selected : nullptr,
+                      exporter ? sa.n_selected : nullptr, exporter ? sa.page_table : nullptr, 1,
+                      MAXB, PT / 8, ssh, prow_lds);
+    pt_lo = lane < PT ? prow_lds[lane] : -1;
+    pt_hi = lane + kWave < PT ? prow_lds[lane + kWave] : -1;
+  } else {
+    const int32_t* prow = page_table + (size_t)r * PT;
+    pt_lo = lane < PT ? prow[lane] : -1;
+    pt_hi = lane + kWave < PT ? prow[lane + kWave] : -1;
+  }
   const int nblk = (__popcll(__ballot(pt_lo >= 0)) + __popcll(__ballot(pt_hi >= 0))) >> 3;
   // keys of the local block that are causal to the row (position L - T + t)
   const int vloc = ((ctx_lens[b] - T + t) & 127) + 1;
@@ -589,17 +612,17 @@ long attention_workgroups(const Dims& d, const SplitPlan& sp) {
   return reqs * d.T * d.Hkv * sp.splits;
 }
 
-template <int KV, int W>
+template <int KV, int W, bool SEL>
 hipError_t launch_kvw(const Dims& d, const SplitPlan& sp, const void* q, const void* k_pool,
                       const void* v_pool, const void* k_scale, const void* v_scale,
                       const int32_t* page_table, const int32_t* ctx_lens, float* part_o,
-                      float* part_ml, float* out, hipStream_t s) {
-  hipLaunchKernelGGL((sparse_attn_kernel<KV, W>),
+                      float* part_ml, float* out, const SelectArgs& sa, hipStream_t s) {
+  hipLaunchKernelGGL((sparse_attn_kernel<KV, W, SEL>),
                      dim3((unsigned)attention_workgroups(d, sp)), dim3(64 * W), 0, s,
                      static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(k_pool),
                      static_cast<const uint8_t*>(v_pool), k_scale, v_scale, page_table,
                      ctx_lens, part_o, part_ml, out, d.B, d.T, d.Hq, d.Hkv, d.PT(), sp.splits,
-                     d.NB - 1, d.scale_log2);
+                     d.NB - 1, d.scale_log2, sa, d.MAXB);
   return hipGetLastError();
 }
 
@@ -607,13 +630,16 @@ template <int KV>
 hipError_t launch_kv(const Dims& d, const SplitPlan& sp, const void* q, const void* k_pool,
                      const void* v_pool, const void* k_scale, const void* v_scale,
                      const int32_t* page_table, const int32_t* ctx_lens, float* part_o,
-                     float* part_ml, float* out, hipStream_t s) {
-#define MSA_ATTN(WV)                                                                      \
-  return launch_kvw<KV, WV>(d, sp, q, k_pool, v_pool, k_scale, v_scale, page_table, ctx_lens, \
-                            part_o, part_ml, out, s)
-  if (sp.waves == 8) MSA_ATTN(8);
-  MSA_ATTN(4);
-#undef MSA_ATTN
+                     float* part_ml, float* out, const SelectArgs* sel, hipStream_t s) {
+  if (sel)
+    return launch_kvw<KV, 8, true>(d, sp, q, k_pool, v_pool, k_scale, v_scale, nullptr,
+                                   ctx_lens, part_o, part_ml, out, *sel, s);
+  const SelectArgs none{};
+  if (sp.waves == 8)
+    return launch_kvw<KV, 8, false>(d, sp, q, k_pool, v_pool, k_scale, v_scale, page_table,
+                                    ctx_lens, part_o, part_ml, out, none, s);
+  return launch_kvw<KV, 4, false>(d, sp, q, k_pool, v_pool, k_scale, v_scale, page_table,
+                                  ctx_lens, part_o, part_ml, out, none, s);
 }
 
 }  // namespace
@@ -633,26 +659,37 @@ SplitPlan plan_splits(const Dims& d) {
   return p;
 }
 
+// Rows of at most this many blocks select inside the attention launch (the
+// 8-wave selection then holds at most 4 candidates per lane).
+constexpr int kFusedSelectMaxBlocks = 2048;
+
+bool fused_select_eligible(const Dims& d) {
+  return d.T == 1 && d.MAXB <= kFusedSelectMaxBlocks && plan_splits(d).waves == 8;
+}
+
 hipError_t launch_sparse_attention(const Dims& d, const void* q, const void* k_pool,
                                    const void* v_pool, const void* k_scale,
                                    const void* v_scale, const int32_t* page_table,
                                    const int32_t* ctx_lens, float* part_o, float* part_ml,
-                                   float* out, hipStream_t s, std::string* note) {
+                                   float* out, hipStream_t s, std::string* note,
+                                   const SelectArgs* sel) {
   const SplitPlan sp = plan_splits(d);
+  if (sel && !fused_select_eligible(d)) return hipErrorInvalidValue;
   hipError_t e;
   if (d.kv_dtype == 0)
     e = launch_kv<0>(d, sp, q, k_pool, v_pool, k_scale, v_scale, page_table, ctx_lens, part_o,
-                     part_ml, out, s);
+                     part_ml, out, sel, s);
   else if (d.kv_dtype == 1)
     e = launch_kv<1>(d, sp, q, k_pool, v_pool, k_scale, v_scale, page_table, ctx_lens, part_o,
-                     part_ml, out, s);
+                     part_ml, out, sel, s);
   else
     e = launch_kv<2>(d, sp, q, k_pool, v_pool, k_scale, v_scale, page_table, ctx_lens, part_o,
-                     part_ml, out, s);
+                     part_ml, out, sel, s);
   if (e != hipSuccess) return e;
   static const char* names[3] = {"bf16", "fp8", "nvfp4"};
   if (note)
-    *note += std::string("sparse_attn<") + names[d.kv_dtype] + ">[grid=" +
+    *note += std::string("sparse_attn<") + names[d.kv_dtype] + ">" +
+             (sel ? "+select_topk" : "") + "[grid=" +
              std::to_string(attention_workgroups(d, sp)) + "x" + std::to_string(64 * sp.waves) +
              ",splits=" + std::to_string(sp.splits) + "]";
   if (sp.splits > 1) {

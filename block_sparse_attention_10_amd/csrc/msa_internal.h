@@ -48,13 +48,31 @@ hipError_t launch_select(const Dims& d, const float* scores, const int32_t* ctx_
 hipError_t launch_page_table(const Dims& d, const int32_t* selected, const int32_t* block_table,
                              int32_t* page_table, hipStream_t s, std::string* note);
 
+// Inputs of the selection an attention workgroup runs itself when the
+// selection is fused into the attention launch (single-row requests).  The
+// (KV head 0, split 0) workgroup of each row exports its selection and page
+// ids to selected / n_selected / page_table when those are not null.
+struct SelectArgs {
+  const float* scores;
+  const int32_t* block_table;
+  int32_t* selected;
+  int32_t* n_selected;
+  int32_t* page_table;
+};
+
+// True when msa_decode selects inside the attention launch for `d`.
+bool fused_select_eligible(const Dims& d);
+
 // One launch when a workgroup covers a whole (row, KV head); otherwise the
-// split partials land in part_o / part_ml and a merge launch follows.
+// split partials land in part_o / part_ml and a merge launch follows.  With
+// `sel` (fused_select_eligible(d) must hold) the workgroups select their
+// row's blocks from the block scores first and page_table is not read.
 hipError_t launch_sparse_attention(const Dims& d, const void* q, const void* k_pool,
                                    const void* v_pool, const void* k_scale,
                                    const void* v_scale, const int32_t* page_table,
                                    const int32_t* ctx_lens, float* part_o, float* part_ml,
-                                   float* out, hipStream_t s, std::string* note);
+                                   float* out, hipStream_t s, std::string* note,
+                                   const SelectArgs* sel = nullptr);
 
 // Pools the write path fills (layouts as the attention reads them).
 struct InsertPools {

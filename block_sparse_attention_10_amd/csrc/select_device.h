@@ -193,7 +193,9 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
 
 // Selection (and, when page_table is given, the page table) for every row of
 // request b.  Called by all threads of an NW-wave workgroup (NW = 8 only for
-// single-row requests); contains workgroup barriers.
+// single-row requests); contains workgroup barriers.  page_row (LDS, single-
+// row requests): the row's page ids are also left there, visible to the
+// whole workgroup on return.
 //
 // Per row: every lane takes the best key among its candidates; each wave
 // finds the K1-th best of its lane maxima (K1 = topk - 1) by counting.  That key has
@@ -211,7 +213,8 @@ __device__ __forceinline__ void select_request(int b, const float* __restrict__ 
                                             int32_t* __restrict__ selected,
                                             int32_t* __restrict__ n_selected,
                                             int32_t* __restrict__ page_table, int T, int MAXB,
-                                            int topk, SelectLds<NW>& sh) {
+                                            int topk, SelectLds<NW>& sh,
+                                            int32_t* page_row = nullptr) {
   const int lane = lane_id();
   const int wave = wave_id();
   const int parts = NW == 8 ? 8 : (T >= 4 ? 1 : (T == 1 ? 4 : (T == 2 ? 2 : 1)));
@@ -448,13 +451,14 @@ __device__ __forceinline__ void select_request(int b, const float* __restrict__ 
         for (int k = lane; k < topk; k += kWave)
           selected[(size_t)r * topk + k] = k < n ? row_sel[wave][k] : -1;
       if (lane == 0 && n_selected) n_selected[r] = n;
-      if (page_table) {
+      if (page_table || page_row) {
         const int pt = topk * 8;
         for (int e = lane; e < pt; e += kWave) {
           const int k = e >> 3;
           int v = -1;
           if (k < n) v = block_table[(size_t)b * MAXB + row_sel[wave][k]] * 8 + (e & 7);
-          page_table[(size_t)r * pt + e] = v;
+          if (page_table) page_table[(size_t)r * pt + e] = v;
+          if (page_row) page_row[e] = v;
         }
       }
     }
