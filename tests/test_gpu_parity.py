@@ -234,3 +234,38 @@ def test_full_workload_parity(name):
     _say(f"full workload {name}: max abs err {err:.3g}")
     del w, got, stages
     torch.cuda.empty_cache()
+
+
+
+@pytest.mark.parametrize("maxb,fused", [(2048, True), (2049, False)])
+def test_selection_inside_attention_up_to_2048_blocks(maxb, fused):
+    """msa_decode selects inside the attention launch for single-row requests
+    whose block table is at most 2048 blocks wide, and in a launch of its own
+    beyond.  The table is widened (valid ids past the contexts) to either
+    side of that edge; both must give the stage-wise entry points' results on
+    the unwidened table bit for bit.  Two KV heads and split rows: every
+    (KV head, split) workgroup of a row selects, one of them exports."""
+    cfg = small_config(batch=3, query_len=1, ctx_lo=9000, ctx_hi=30000, num_q_heads=16,
+                       num_kv_heads=2, num_idx_heads=2, n_plant=4, seed=31)
+    print(f"fused-selection edge: table width {maxb}", flush=True)
+    w = make_workload(cfg, DEV)
+    ref = run_stages(w)
+    t = w.tensors
+    wide = torch.zeros((cfg.batch, maxb), dtype=torch.int32, device=DEV)
+    wide[:, :t["block_table"].shape[1]] = t["block_table"]
+    p, tt = msa.describe(t["q"], t["idx_q"], t["k_pool"], t["v_pool"], t["k_scale"],
+                         t["v_scale"], t["idx_k_pool"], wide, t["ctx_lens"],
+                         decode_query_len=1, topk=cfg.topk, idx_k_scale=t.get("idx_k_scale"))
+    sel = torch.empty_like(ref["selected"])
+    pt = torch.empty_like(ref["page_table"])
+    out = torch.empty_like(ref["out"])
+    ws = torch.empty((msa.msa_workspace_bytes(p),), dtype=torch.uint8, device=DEV)
+    msa.msa_decode(p, tt, sel, pt, out, ws)
+    torch.cuda.synchronize()
+    rec = msa.msa_last_dispatch()
+    assert ("sparse_attn<bf16>+select_topk" in rec) == fused, rec
+    assert (" select_topk[" in rec) != fused, rec
+    assert torch.equal(sel, ref["selected"])
+    assert torch.equal(pt, ref["page_table"])
+    assert torch.equal(out, ref["out"])
+    assert compare_rows(w, ref, list(range(cfg.rows))) <= TOL[cfg.kv_dtype]
