@@ -7,6 +7,9 @@
 //
 //   msa_counters scan   <spec> <launches>   msa_index_score x launches
 //   msa_counters decode <spec> <launches>   msa_decode x launches
+//   msa_counters decode <spec> <launches> flush
+//                                           each msa_decode after a 1 GiB copy
+//                                           (caches and TLBs hold other data)
 //   msa_counters copy   <MiB>  <launches>   16-byte copy kernel x launches
 //
 // Index keys and queries hold hashed small integers in [-8, 8] (so the
@@ -96,8 +99,10 @@ static int dtype_code(const std::string& s) {
 }
 
 int main(int argc, char** argv) {
-  if (argc != 4) {
-    fprintf(stderr, "usage: %s scan|decode <spec> <launches> | copy <MiB> <launches>\n",
+  const bool flush = argc == 5 && std::string(argv[4]) == "flush";
+  if (argc != 4 && !flush) {
+    fprintf(stderr,
+            "usage: %s scan|decode <spec> <launches> [flush] | copy <MiB> <launches>\n",
             argv[0]);
     return 2;
   }
@@ -220,7 +225,13 @@ int main(int argc, char** argv) {
     ws = dalloc(ws_bytes);
     out = (float*)dalloc(R * Hq * 128 * 4);
   }
+  const size_t flush_bytes = (size_t)1 << 30;
+  void* flush_a = flush ? dalloc(flush_bytes) : nullptr;
+  void* flush_b = flush ? dalloc(flush_bytes) : nullptr;
   for (int i = 0; i < launches; ++i) {
+    if (flush)
+      hipLaunchKernelGGL(copy16, dim3(4096), dim3(256), 0, 0, (const u32x4*)flush_a,
+                         (u32x4*)flush_b, flush_bytes / 16);
     const int st = mode == "scan" ? msa_index_score(&p, &t, scores, nullptr)
                                   : msa_decode(&p, &t, nullptr, nullptr, out, ws, ws_bytes, nullptr);
     if (st != MSA_OK) {
