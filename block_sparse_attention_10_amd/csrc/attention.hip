@@ -659,9 +659,11 @@ SplitPlan plan_splits(const Dims& d) {
   return p;
 }
 
-// Rows of at most this many blocks select inside the attention launch (the
-// 8-wave selection then holds at most 4 candidates per lane).
-constexpr int kFusedSelectMaxBlocks = 2048;
+// Rows of at most this many blocks select inside the attention launch.
+// Every workgroup of a row reads the row's scores (64 KB at this bound);
+// measured on MI355X the fused launch is faster up to the 1M context (8192
+// blocks: 177 vs 181 us per step, 182.5 vs 187.7 after a cache flush).
+constexpr int kFusedSelectMaxBlocks = 16384;
 
 bool fused_select_eligible(const Dims& d) {
   return d.T == 1 && d.MAXB <= kFusedSelectMaxBlocks && plan_splits(d).waves == 8;

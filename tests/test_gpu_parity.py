@@ -237,10 +237,10 @@ def test_full_workload_parity(name):
 
 
 
-@pytest.mark.parametrize("maxb,fused", [(2048, True), (2049, False)])
-def test_selection_inside_attention_up_to_2048_blocks(maxb, fused):
+@pytest.mark.parametrize("maxb,fused", [(16384, True), (16385, False)])
+def test_selection_inside_attention_up_to_16384_blocks(maxb, fused):
     """msa_decode selects inside the attention launch for single-row requests
-    whose block table is at most 2048 blocks wide, and in a launch of its own
+    whose block table is at most 16384 blocks wide, and in a launch of its own
     beyond.  The table is widened (valid ids past the contexts) to either
     side of that edge; both must give the stage-wise entry points' results on
     the unwidened table bit for bit.  Two KV heads and split rows: every
