@@ -257,7 +257,7 @@ int msa_decode(const msa_problem* p, const msa_tensors* t, int32_t* selected,
   // Single-row requests select inside the attention launch (one launch
   // fewer on the dependent chain); the rest select in a launch of their own.
   const bool fuse = fused_select_eligible(d);
-  const SelectArgs fused{scores, t->block_table, selected, selected ? nsel : nullptr, page_table};
+  const SelectArgs fused{scores, t->block_table, selected, nullptr, page_table};
   if (!fuse) {
     if ((e = hip_status(launch_select(d, scores, t->ctx_lens, t->block_table, sel, nsel, pt, s,
                                       &note))))
