@@ -62,6 +62,10 @@ SMALL = [
          num_q_heads=16, num_kv_heads=2, seed=24),
     dict(batch=2, query_len=5, ctx_lo=300, ctx_hi=6000, idx_dtype="nvfp4", kv_dtype="fp8",
          seed=25),
+    # single rows around the take-every-block edge (16 blocks = 2048 tokens),
+    # where msa_decode selects inside the attention launch
+    dict(batch=8, query_len=1, ctx_list=(1, 127, 128, 129, 2047, 2048, 2049, 2177),
+         num_q_heads=16, num_kv_heads=2, seed=26),
 ]
 
 
@@ -81,8 +85,9 @@ def test_small_shapes_stagewise_and_fused(kw):
     _say(f"  max abs err {err:.3g} (tol {TOL[cfg.kv_dtype]})")
 
 
-def test_fused_without_exported_tables():
-    cfg = small_config(batch=3, query_len=2, ctx_lo=3000, ctx_hi=9000, seed=12)
+@pytest.mark.parametrize("T", [1, 2])
+def test_fused_without_exported_tables(T):
+    cfg = small_config(batch=3, query_len=T, ctx_lo=3000, ctx_hi=9000, seed=12)
     w = make_workload(cfg, DEV)
     a = run_fused(w, export=True)
     b = run_fused(w, export=False)
