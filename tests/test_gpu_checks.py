@@ -19,8 +19,8 @@ DEV = "cuda"
 BAD = 1  # the request whose inputs are broken
 
 
-def padded_workload(**kw):
-    cfg = small_config(batch=3, query_len=2, ctx_lo=1500, ctx_hi=3000, seed=31, **kw)
+def padded_workload(query_len=2, **kw):
+    cfg = small_config(batch=3, query_len=query_len, ctx_lo=1500, ctx_hi=3000, seed=31, **kw)
     w = make_workload(cfg, DEV)
     keep = {}
     t = dict(w.tensors)
@@ -71,8 +71,11 @@ def untouched(o, *names):
         assert bool((x == 7).all()), f"{n} was written after a failed check"
 
 
-def test_valid_inputs_pass_and_give_the_same_results():
-    w, t, keep = padded_workload()
+# one row per request: msa_decode selects inside its attention launch; two:
+# in a selection launch of its own
+@pytest.mark.parametrize("T", [1, 2])
+def test_valid_inputs_pass_and_give_the_same_results(T):
+    w, t, keep = padded_workload(query_len=T)
     res = {}
     for flags in (0, msa.MSA_FLAG_DEBUG_CHECKS):
         p, tt = describe(w, t, flags=flags)
@@ -94,9 +97,10 @@ def test_valid_inputs_pass_and_give_the_same_results():
     assert torch.equal(a["out"], fa)
 
 
+@pytest.mark.parametrize("T", [1, 2])
 @pytest.mark.parametrize("bad_len", ["short", "long"])
-def test_bad_context_length_is_reported_before_any_launch(bad_len):
-    w, t, keep = padded_workload()
+def test_bad_context_length_is_reported_before_any_launch(bad_len, T):
+    w, t, keep = padded_workload(query_len=T)
     c = w.cfg
     ctx = t["ctx_lens"].clone()
     ctx[BAD] = c.query_len - 1 if bad_len == "short" else c.max_blocks * 128 + 1
@@ -112,9 +116,10 @@ def test_bad_context_length_is_reported_before_any_launch(bad_len):
     untouched(o, "scores", "selected", "n_selected", "page_table", "out")
 
 
+@pytest.mark.parametrize("T", [1, 2])
 @pytest.mark.parametrize("value", ["minus_one", "nb"])
-def test_bad_table_entry_inside_the_context_is_reported(value):
-    w, t, keep = padded_workload()
+def test_bad_table_entry_inside_the_context_is_reported(value, T):
+    w, t, keep = padded_workload(query_len=T)
     c = w.cfg
     L = int(t["ctx_lens"][BAD])
     col = (L - 1) // 128 // 2  # an older block of the context
@@ -130,8 +135,9 @@ def test_bad_table_entry_inside_the_context_is_reported(value):
     untouched(o, "scores", "out")
 
 
-def test_table_entries_past_the_context_are_not_checked():
-    w, t, keep = padded_workload()
+@pytest.mark.parametrize("T", [1, 2])
+def test_table_entries_past_the_context_are_not_checked(T):
+    w, t, keep = padded_workload(query_len=T)
     c = w.cfg
     L = int(t["ctx_lens"][BAD])
     last = (L - 1) // 128
