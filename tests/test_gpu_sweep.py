@@ -10,6 +10,8 @@ selection, split and unsplit attention) in combinations the hand-picked
 shapes do not.  Same bar as the other parity tests: scores, selections and
 page tables bit for bit, outputs within 2e-3 (bf16 KV) or 1e-2.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -44,7 +46,10 @@ def _draw(n, seed=20261202):
     return out
 
 
-CASES = _draw(24)
+# MSA_SWEEP_CASES / MSA_SWEEP_SEED widen the sweep for a longer run, e.g.
+# MSA_SWEEP_CASES=600 MSA_SWEEP_SEED=4242 python -m pytest tests/test_gpu_sweep.py
+CASES = _draw(int(os.environ.get("MSA_SWEEP_CASES", "24")),
+              seed=int(os.environ.get("MSA_SWEEP_SEED", "20261202")))
 
 
 def _id(kw):
