@@ -1,5 +1,5 @@
 """Helpers for the GPU tests: run the library through its C ABI on a
-synthetic workload, and compute oracle results for sampled rows.
+synthetic workload, and compute oracle results for any set of rows.
 
 The oracle side only ever sees generator outputs (gathered on the device by
 torch indexing and copied to the host) and its own selections; nothing the
@@ -83,52 +83,64 @@ def _host(x: torch.Tensor) -> np.ndarray:
     return x.numpy()
 
 
+def _compact(pool, phys):
+    """Host copy of the blocks `phys` (int64 device tensor) of a pool."""
+    return None if pool is None else _host(pool[phys])
+
+
 def oracle_rows(w: Workload, rows):
-    """Oracle results for the given rows, computed request by request on
-    compact host copies of just the blocks the oracle needs."""
+    """Oracle results for the given rows, in one oracle call per step so that
+    its OpenMP loops spread over all the rows.  The index keys of the rows'
+    requests (every block of their contexts) and the K/V blocks the oracle
+    selects are copied to compact host pools; the block tables are remapped
+    to them, so the oracle never reads the rest of the device pools."""
     c = w.cfg
     T = c.query_len
     t = w.tensors
-    bt_all = t["block_table"]
-    res = {}
-    by_req = {}
-    for r in rows:
-        by_req.setdefault(r // T, []).append(r)
-    for b, rs in by_req.items():
-        L = w.ctx_lens[b]
-        nblk = w.nblk[b]
-        bt_row = bt_all[b, :nblk].to(torch.int64)
-        local_rows = np.array([r % T for r in rs], dtype=np.int32)
-        mini = problem_of(c)
-        mini.batch = 1
-        mini.max_blocks = nblk
-        iks = t.get("idx_k_scale")
-        idx = {
-            "idx_q": _host(t["idx_q"][b * T:(b + 1) * T]),
-            "idx_k_pool": _host(t["idx_k_pool"][bt_row]),
-            "idx_k_scale": None if iks is None else _host(iks[bt_row]),
-            "bt": np.arange(nblk, dtype=np.int32)[None, :],
-            "ctx": np.array([L], dtype=np.int32),
-        }
-        s = oracle.index_scores(mini, idx["idx_q"], idx["idx_k_pool"], idx["bt"], idx["ctx"],
-                                local_rows, idx_k_scale=idx["idx_k_scale"])
-        sel, nsel = oracle.select(mini, s, idx["ctx"], local_rows)
-        pt = oracle.page_table(mini, sel, _host(bt_all[b:b + 1, :nblk]), local_rows)
-        # attention on a pool holding only the selected blocks
-        used = sorted({int(x) for x in sel.reshape(-1) if x >= 0})
-        remap = np.zeros(nblk, dtype=np.int32)
-        remap[used] = np.arange(len(used), dtype=np.int32)
-        phys = bt_row[torch.tensor(used, dtype=torch.int64, device=bt_row.device)]
-        kv = {}
-        for name in ("k_pool", "v_pool", "k_scale", "v_scale"):
-            kv[name] = None if t[name] is None else _host(t[name][phys])
-        out = oracle.attention(mini, _host(t["q"][b * T:(b + 1) * T]), kv["k_pool"],
-                               kv["v_pool"], kv["k_scale"], kv["v_scale"], remap[None, :],
-                               idx["ctx"], sel, local_rows)
-        for i, r in enumerate(rs):
-            res[r] = {"scores": s[i], "selected": sel[i], "n_selected": int(nsel[i]),
-                      "page_table": pt[i], "out": out[i]}
-    return res
+    rows = [int(r) for r in rows]
+    reqs = sorted({r // T for r in rows})
+    bt_host = _host(t["block_table"]).astype(np.int64)
+    ctx = np.asarray(w.ctx_lens, dtype=np.int32)
+    prob = problem_of(c)
+    rows_np = np.asarray(rows, dtype=np.int32)
+
+    # compact index-key pool: the context blocks of the rows' requests
+    phys_list, bt_idx = [], np.zeros(bt_host.shape, dtype=np.int32)
+    off = 0
+    for b in reqs:
+        n = w.nblk[b]
+        phys_list.append(bt_host[b, :n])
+        bt_idx[b, :n] = np.arange(off, off + n, dtype=np.int32)
+        off += n
+    phys = torch.from_numpy(np.concatenate(phys_list)).to(t["block_table"].device)
+    ik = _compact(t["idx_k_pool"], phys)
+    iks = _compact(t.get("idx_k_scale"), phys)
+    del phys
+    s = oracle.index_scores(prob, _host(t["idx_q"]), ik, bt_idx, ctx, rows_np, idx_k_scale=iks)
+    del ik, iks
+    sel, nsel = oracle.select(prob, s, ctx, rows_np)
+    pt = oracle.page_table(prob, sel, bt_host.astype(np.int32), rows_np)
+
+    # attention on a pool holding only the selected blocks (all rows at once)
+    bt_kv = np.zeros(bt_host.shape, dtype=np.int32)
+    used = {}
+    for i, r in enumerate(rows):
+        b = r // T
+        for x in sel[i]:
+            if x >= 0:
+                key = int(bt_host[b, x])
+                if key not in used:
+                    used[key] = len(used)
+                bt_kv[b, x] = used[key]
+    order = np.empty(len(used), dtype=np.int64)
+    for key, j in used.items():
+        order[j] = key
+    phys = torch.from_numpy(order).to(t["block_table"].device)
+    kv = {name: _compact(t[name], phys) for name in ("k_pool", "v_pool", "k_scale", "v_scale")}
+    out = oracle.attention(prob, _host(t["q"]), kv["k_pool"], kv["v_pool"], kv["k_scale"],
+                           kv["v_scale"], bt_kv, ctx, sel, rows_np)
+    return {r: {"scores": s[i][:w.nblk[r // T]], "selected": sel[i], "n_selected": int(nsel[i]),
+                "page_table": pt[i], "out": out[i]} for i, r in enumerate(rows)}
 
 
 def oracle_attention_rows(w: Workload, rows, selection):

@@ -201,12 +201,12 @@ def test_workspace_too_small_is_rejected():
 
 
 # --------------------------------------------------------- full workloads
-SAMPLE_ROWS = {"tiny_4k": None, "tp8_rank_32k": 6, "layer_128k": 6, "spec_verify_fp8": 12,
-               "ctx_1m_nvfp4": 4, "layer_128k_nvfp4_index": 6}
-
-
 @pytest.mark.parametrize("name", CONFIG_ORDER + EXTRA_CONFIGS)
 def test_full_workload_parity(name):
+    """Every row of every full-size workload against the oracle: block
+    scores, selections, counts and page tables bit for bit, outputs within
+    the tolerance (the 16-block / 2,048-key selection holds for every query,
+    aisoku.org article, section "MSAの仕組み")."""
     cfg = CONFIGS[name]
     _say(f"full workload {name}: generating")
     w = make_workload(cfg, DEV)
@@ -218,15 +218,10 @@ def test_full_workload_parity(name):
         assert torch.equal(got[k], stages[k]), f"{name}: fused {k} differs from stage-wise"
     got["scores"] = stages["scores"]
     got["n_selected"] = stages["n_selected"]
+    del stages
     check_invariants(w, got)
-    n = SAMPLE_ROWS[name]
-    if n is None:
-        rows = list(range(cfg.rows))
-    else:
-        rng = np.random.default_rng(cfg.seed)
-        rows = sorted(set(int(x) for x in rng.choice(cfg.rows, size=n, replace=False)) |
-                      {0, cfg.rows - 1})
-    _say(f"full workload {name}: oracle on rows {rows}")
+    rows = list(range(cfg.rows))
+    _say(f"full workload {name}: oracle on all {len(rows)} rows")
     err = compare_rows(w, got, rows)
     # planted blocks are kept for every row 0 of a request
     if cfg.n_plant and cfg.query_len == 1:
@@ -236,10 +231,10 @@ def test_full_workload_parity(name):
                 assert set(w.planted[b]) <= set(sel[b].tolist()), f"request {b}"
             else:
                 assert len(set(w.planted[b]) & set(sel[b].tolist())) == cfg.topk - 1
-    _say(f"full workload {name}: max abs err {err:.3g}")
-    del w, got, stages
+    _say(f"full workload {name}: {len(rows)} rows match, max abs err {err:.3g} "
+         f"(tol {TOL[cfg.kv_dtype]})")
+    del w, got
     torch.cuda.empty_cache()
-
 
 
 @pytest.mark.parametrize("maxb,fused", [(16384, True), (16385, False)])
