@@ -188,7 +188,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--export-spec", default=None,
                     help="write the workload's shapes, contexts and block table for the "
-                         "counter driver (block_sparse_attention_10_amd/driver) and exit")
+                         "counter driver (msa_counters.cpp) and exit")
     args = ap.parse_args()
 
     if args.export_spec:

@@ -19,8 +19,6 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmsa.so")
-DRIVER_SRC = os.path.join(PKG, "driver", "msa_counters.cpp")
-DRIVER = os.path.join(PKG, "driver", "msa_counters")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -55,14 +53,20 @@ def build(verbose: bool = False, extra_flags=()) -> str:
     tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, LIB)
-    # the counter driver: a torch-free process for rocprofv3 --pmc runs
-    tmp = DRIVER + ".tmp"
-    _run([HIPCC, *FLAGS, *extra_flags, DRIVER_SRC, "-o", tmp, "-L", PKG, "-lmsa",
-          "-Wl,-rpath,$ORIGIN/.."])
-    os.replace(tmp, DRIVER)
     if verbose:
-        print("built", LIB, "and", DRIVER)
+        print("built", LIB)
     return LIB
+
+
+def build_counter_driver(src: str, exe: str) -> str:
+    """The torch-free driver of the rocprofv3 counter runs (a measurement
+    tool, not part of the library), linked against the built libmsa.so; the
+    run path is relative to the executable, so the tree can move."""
+    rel = os.path.relpath(PKG, os.path.dirname(os.path.abspath(exe)))
+    tmp = exe + ".tmp"
+    _run([HIPCC, *FLAGS, src, "-o", tmp, "-L", PKG, "-lmsa", "-Wl,-rpath,$ORIGIN/" + rel])
+    os.replace(tmp, exe)
+    return exe
 
 
 if __name__ == "__main__":

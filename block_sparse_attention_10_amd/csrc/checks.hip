@@ -2,9 +2,9 @@
 // descriptor sets MSA_FLAG_DEBUG_CHECKS.
 //
 // The fast path trusts ctx_lens, the block table, selections handed to the
-// page-table build and page tables handed to the attention: a context
-// longer than the table row or a table entry outside the pools sends the
-// scan, the selection or the write path outside its buffers.  In debug mode
+// page-table build and page tables handed to the attention for its results
+// (the kernels clamp the block ids they dereference, so a bad entry reads
+// or writes the wrong place inside the caller's buffers).  In debug mode
 // one workgroup reads those inputs, records the first violation of each
 // kind, and the host reads the record back (the call synchronises its
 // stream) before anything else is launched, so a bad input is reported and

@@ -317,7 +317,7 @@ __global__ __launch_bounds__(256) void index_scan_kernel(
     const uint16_t* __restrict__ idx_q, const uint8_t* __restrict__ idx_k,
     const uint8_t* __restrict__ idx_ks, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ ctx_lens, float* __restrict__ scores, int B, int T, int Hidx,
-    int MAXB) {
+    int MAXB, int max_block) {
   const int lane = lane_id();
   const int item = blockIdx.x * 4 + wave_id();
   if (item >= B * MAXB) return;
@@ -328,6 +328,7 @@ __global__ __launch_bounds__(256) void index_scan_kernel(
   int phys = block_table[(size_t)b * MAXB + c];
   const int L = ctx_lens[b];
   asm volatile("" : "+s"(phys));  // keeps the table load ahead of the branch
+  phys = min(max(phys, 0), max_block);  // a bad table entry cannot leave the pool
   if (c * kBlock > L - 1) {
     float* srow = scores + (size_t)b * T * MAXB + c;
     for (int t = lane; t < T; t += kWave) srow[(size_t)t * MAXB] = -INFINITY;
@@ -380,17 +381,17 @@ hipError_t launch_kind(const Dims& d, const void* idx_q, const void* idx_k, cons
   if constexpr (KIND != kFp4) {
     if (tr == 0)
       hipLaunchKernelGGL((index_scan_kernel<KIND, 0>), grid, block, lds, s, q, k, ks, bt, cl,
-                         scores, d.B, d.T, d.Hidx, d.MAXB);
+                         scores, d.B, d.T, d.Hidx, d.MAXB, d.NB - 1);
   }
   if (tr == 1)
     hipLaunchKernelGGL((index_scan_kernel<KIND, 1>), grid, block, lds, s, q, k, ks, bt, cl, scores,
-                       d.B, d.T, d.Hidx, d.MAXB);
+                       d.B, d.T, d.Hidx, d.MAXB, d.NB - 1);
   else if (tr == 2)
     hipLaunchKernelGGL((index_scan_kernel<KIND, 2>), grid, block, lds, s, q, k, ks, bt, cl, scores,
-                       d.B, d.T, d.Hidx, d.MAXB);
+                       d.B, d.T, d.Hidx, d.MAXB, d.NB - 1);
   else if (tr == 4)
     hipLaunchKernelGGL((index_scan_kernel<KIND, 4>), grid, block, lds, s, q, k, ks, bt, cl, scores,
-                       d.B, d.T, d.Hidx, d.MAXB);
+                       d.B, d.T, d.Hidx, d.MAXB, d.NB - 1);
   static const char* names[3] = {"bf16", "fp8", "nvfp4"};
   if (note)
     *note += std::string("index_scan<") + names[KIND] +

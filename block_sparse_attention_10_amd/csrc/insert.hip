@@ -70,7 +70,7 @@ __global__ __launch_bounds__(256) void insert_kernel(
     const int32_t* __restrict__ ctx_lens, uint8_t* __restrict__ k_pool,
     uint8_t* __restrict__ v_pool, uint8_t* __restrict__ k_scale, uint8_t* __restrict__ v_scale,
     uint8_t* __restrict__ idx_k, uint8_t* __restrict__ idx_ks, int R, int T, int Hkv, int Hidx,
-    int MAXB) {
+    int MAXB, int max_block) {
   const int lane = lane_id();
   const int per = 2 * Hkv + Hidx;
   const long item = (long)blockIdx.x * 4 + wave_id();
@@ -79,7 +79,9 @@ __global__ __launch_bounds__(256) void insert_kernel(
   const int j = (int)(item - (long)r * per);
   const int b = r / T;
   const int pos = ctx_lens[b] - T + (r - b * T);
-  const size_t phys = (size_t)block_table[(size_t)b * MAXB + pos / 128];
+  // a bad context length or table entry cannot leave the table or the pools
+  const int lb = min(max(pos >> 7, 0), MAXB - 1);
+  const size_t phys = (size_t)min(max(block_table[(size_t)b * MAXB + lb], 0), max_block);
   const int slot = pos & 127;
 
   if (j < 2 * Hkv) {
@@ -141,7 +143,7 @@ hipError_t launch_typed(const Dims& d, const void* k_new, const void* v_new,
                      static_cast<uint8_t*>(pl.k_pool), static_cast<uint8_t*>(pl.v_pool),
                      static_cast<uint8_t*>(pl.k_scale), static_cast<uint8_t*>(pl.v_scale),
                      static_cast<uint8_t*>(pl.idx_k_pool), static_cast<uint8_t*>(pl.idx_k_scale),
-                     d.R(), d.T, d.Hkv, d.Hidx, d.MAXB);
+                     d.R(), d.T, d.Hkv, d.Hidx, d.MAXB, d.NB - 1);
   return hipGetLastError();
 }
 

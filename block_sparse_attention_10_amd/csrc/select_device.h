@@ -242,6 +242,9 @@ __device__ __forceinline__ void select_request(int b, const float* __restrict__ 
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) asm volatile("" : "+v"(sv[u]));
     asm volatile("" : "+s"(L));
+    // a context longer than its table row cannot send the candidates (and
+    // the table lookups of the page build) past the row
+    L = min(L, MAXB * 128);
     const bool active = t < T;
     const int r = b * T + t;
     const float* srow = scores + (size_t)r * MAXB;

@@ -43,7 +43,8 @@ __global__ __launch_bounds__(256) void page_table_kernel(const int32_t* __restri
   const int slot = (int)(e - (long)r * pt);
   const int c = selected[(size_t)r * topk + (slot >> 3)];
   int v = -1;
-  if (c >= 0) v = block_table[(size_t)(r / T) * MAXB + c] * 8 + (slot & 7);
+  // a selected id past the table row reads the row's last entry
+  if (c >= 0) v = block_table[(size_t)(r / T) * MAXB + min(c, MAXB - 1)] * 8 + (slot & 7);
   page_table[e] = v;
 }
 

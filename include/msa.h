@@ -76,7 +76,10 @@
  *    exception crosses this boundary.
  *  - Data-dependent inputs (ctx_lens outside the bounds above, block_table
  *    entries outside [0, NB), selections or page tables not of the form
- *    described) are not checked by default and are undefined behaviour.
+ *    described) are not checked by default and give undefined results.
+ *    The kernels clamp every physical block id they dereference to [0, NB)
+ *    and every logical block to the table row, so such inputs read or write
+ *    wrong entries of the caller's pools but no memory outside them.
  *    With flags = MSA_FLAG_DEBUG_CHECKS every call first checks, on the
  *    device, the ctx_lens, block_table entries, selected ids and page-table
  *    rows it reads (for the write path: the table entries of the new

@@ -53,7 +53,10 @@ __global__ void fill_u16(uint16_t* p, size_t n, uint16_t v) {
 }
 
 // Integers in [-8, 8] from a 32-bit hash of the element index, stored as
-// bf16 (BYTES == 2) or e4m3 codes (BYTES == 1); both are exact.
+// bf16 (BYTES == 2) or e4m3 codes (BYTES == 1); both are exact.  The hash
+// is Chris Wellons' published "lowbias32" integer mixer (hash-prospector
+// project: xorshift 16, multiply 0x7feb352d, xorshift 15, multiply
+// 0x846ca68b, xorshift 16).
 __device__ uint32_t hash32(uint32_t x) {
   x ^= x >> 16; x *= 0x7feb352dU; x ^= x >> 15; x *= 0x846ca68bU; x ^= x >> 16;
   return x;

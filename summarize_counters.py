@@ -23,8 +23,8 @@ import os
 import re
 import sys
 
-PKG = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-CSRC = os.path.join(PKG, "csrc")
+ROOT = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(ROOT, "block_sparse_attention_10_amd", "csrc")
 
 # kernel family -> the sources that define it
 SOURCES = {
