@@ -32,7 +32,9 @@ DTYPES = {"bf16": 0, "fp8": 1, "nvfp4": 2}
 EXPORTS = ("msa_index_score", "msa_select_blocks", "msa_build_page_table", "msa_sparse_decode",
            "msa_decode", "msa_workspace_bytes", "msa_status_string", "msa_last_hip_error",
            "msa_last_dispatch", "msa_selftest_decoders", "msa_insert_kv",
-           "msa_last_check_failure")
+           "msa_last_check_failure", "msa_decode_noalloc")
+
+MSA_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 class MSAError(RuntimeError):
@@ -93,6 +95,7 @@ def _load():
             ("msa_build_page_table", [pp, vp, vp, vp, vp]),
             ("msa_sparse_decode", [pp, tp, vp, vp, vp, sz, vp]),
             ("msa_decode", [pp, tp, vp, vp, vp, vp, sz, vp]),
+            ("msa_decode_noalloc", [pp, tp, vp, vp, vp, vp]),
             ("msa_selftest_decoders", [vp, vp]),
             ("msa_insert_kv", [pp, ctypes.POINTER(Pools), vp, vp, vp, vp, vp, vp])):
         f = getattr(L, name)
@@ -217,6 +220,12 @@ def msa_decode(p: Problem, t: Tensors, selected, page_table, out, workspace, str
     _check(_lib.msa_decode(ctypes.byref(p), ctypes.byref(t), _p(selected), _p(page_table),
                            _p(out), _p(workspace), workspace.numel() * workspace.element_size(),
                            _stream(stream)), "msa_decode")
+
+
+def msa_decode_noalloc(p: Problem, t: Tensors, selected, page_table, out, stream=None):
+    _check(_lib.msa_decode_noalloc(ctypes.byref(p), ctypes.byref(t), _p(selected),
+                                   _p(page_table), _p(out), _stream(stream)),
+           "msa_decode_noalloc")
 
 
 def msa_workspace_bytes(p: Problem) -> int:

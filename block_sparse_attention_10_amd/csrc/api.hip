@@ -6,7 +6,20 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
 #include <string>
+
+// The workspace of msa_decode_noalloc, for callers that cannot allocate
+// device memory.  Each device the library runs on holds its own copy until
+// the process ends.  In host code the array's name is only a stand-in for
+// the symbol, never a device address: the address comes from
+// hipGetSymbolAddress, taken once per device with that device current and
+// kept per device (scratch_of_current_device), and only that address is
+// handed to kernels.  The kernels write every workspace byte before they
+// read it, so the array needs no clearing between calls; calls that overlap
+// on one device share it and race.
+static __device__ __align__(256) uint8_t scratch[MSA_NOALLOC_SCRATCH_BYTES];
 
 namespace msa {
 
@@ -140,6 +153,77 @@ int debug_checks(const Dims& d, const int32_t* ctx_lens, const int32_t* block_ta
   return MSA_OK;
 }
 
+// msa_decode on a workspace already validated for presence: the index scan,
+// the selection (its own launch, or inside the attention launch for
+// single-row requests), the attention and its merge.
+int decode_with_workspace(const Dims& d, const msa_tensors* t, int32_t* selected,
+                          int32_t* page_table, float* out, void* workspace,
+                          size_t workspace_bytes, hipStream_t s) {
+  int e;
+  if ((e = check_index_inputs(d, t)) || (e = check_kv_inputs(d, t)) || (e = check_ptr(out)))
+    return e;
+  if ((selected && !aligned16(selected)) || (page_table && !aligned16(page_table)))
+    return MSA_ERR_INVALID_ARG;
+  const Workspace w = workspace_layout(d);
+  if (workspace_bytes < w.total) return MSA_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  float* scores = reinterpret_cast<float*>(ws + w.scores);
+  int32_t* nsel = reinterpret_cast<int32_t*>(ws + w.n_selected);
+  int32_t* sel = selected ? selected : reinterpret_cast<int32_t*>(ws + w.selected);
+  int32_t* pt = page_table ? page_table : reinterpret_cast<int32_t*>(ws + w.page_table);
+  std::string note;
+  if ((e = debug_checks(d, t->ctx_lens, t->block_table, nullptr, nullptr, false, s, &note)))
+    return e;
+  if ((e = hip_status(launch_index_scan(d, t->idx_q, t->idx_k_pool, t->idx_k_scale,
+                                        t->block_table, t->ctx_lens, scores, s, &note))))
+    return e;
+  note += " ";
+  // Single-row requests select inside the attention launch (one launch
+  // fewer on the dependent chain); the rest select in a launch of their own.
+  const bool fuse = fused_select_eligible(d);
+  const SelectArgs fused{scores, t->block_table, selected, nullptr, page_table};
+  if (!fuse) {
+    if ((e = hip_status(launch_select(d, scores, t->ctx_lens, t->block_table, sel, nsel, pt, s,
+                                      &note))))
+      return e;
+    note += " ";
+  }
+  if ((e = hip_status(launch_sparse_attention(d, t->q, t->k_pool, t->v_pool, t->k_scale,
+                                              t->v_scale, pt, t->ctx_lens,
+                                              reinterpret_cast<float*>(ws + w.part_o),
+                                              reinterpret_cast<float*>(ws + w.part_ml), out, s,
+                                              &note, fuse ? &fused : nullptr))))
+    return e;
+  g_last_dispatch = note;
+  return MSA_OK;
+}
+
+// ---- the workspace of msa_decode_noalloc (the array `scratch` above)
+constexpr size_t kScratchBytes = MSA_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+hipError_t scratch_of_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(::scratch));
+      if (e != hipSuccess) return e;
+      if (!p) return hipErrorInvalidSymbol;
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
+
 }  // namespace
 }  // namespace msa
 
@@ -234,44 +318,21 @@ int msa_decode(const msa_problem* p, const msa_tensors* t, int32_t* selected,
   Dims d;
   int e;
   if ((e = check_problem(p, &d))) return e;
-  if ((e = check_index_inputs(d, t)) || (e = check_kv_inputs(d, t)) || (e = check_ptr(out)) ||
-      (e = check_ptr(workspace)))
-    return e;
-  if ((selected && !aligned16(selected)) || (page_table && !aligned16(page_table)))
-    return MSA_ERR_INVALID_ARG;
-  const Workspace w = workspace_layout(d);
-  if (workspace_bytes < w.total) return MSA_ERR_WORKSPACE;
-  char* ws = static_cast<char*>(workspace);
-  float* scores = reinterpret_cast<float*>(ws + w.scores);
-  int32_t* nsel = reinterpret_cast<int32_t*>(ws + w.n_selected);
-  int32_t* sel = selected ? selected : reinterpret_cast<int32_t*>(ws + w.selected);
-  int32_t* pt = page_table ? page_table : reinterpret_cast<int32_t*>(ws + w.page_table);
-  hipStream_t s = (hipStream_t)stream;
-  std::string note;
-  if ((e = debug_checks(d, t->ctx_lens, t->block_table, nullptr, nullptr, false, s, &note)))
-    return e;
-  if ((e = hip_status(launch_index_scan(d, t->idx_q, t->idx_k_pool, t->idx_k_scale,
-                                        t->block_table, t->ctx_lens, scores, s, &note))))
-    return e;
-  note += " ";
-  // Single-row requests select inside the attention launch (one launch
-  // fewer on the dependent chain); the rest select in a launch of their own.
-  const bool fuse = fused_select_eligible(d);
-  const SelectArgs fused{scores, t->block_table, selected, nullptr, page_table};
-  if (!fuse) {
-    if ((e = hip_status(launch_select(d, scores, t->ctx_lens, t->block_table, sel, nsel, pt, s,
-                                      &note))))
-      return e;
-    note += " ";
-  }
-  if ((e = hip_status(launch_sparse_attention(d, t->q, t->k_pool, t->v_pool, t->k_scale,
-                                              t->v_scale, pt, t->ctx_lens,
-                                              reinterpret_cast<float*>(ws + w.part_o),
-                                              reinterpret_cast<float*>(ws + w.part_ml), out, s,
-                                              &note, fuse ? &fused : nullptr))))
-    return e;
-  g_last_dispatch = note;
-  return MSA_OK;
+  if ((e = check_ptr(workspace))) return e;
+  return decode_with_workspace(d, t, selected, page_table, out, workspace, workspace_bytes,
+                               (hipStream_t)stream);
+}
+
+int msa_decode_noalloc(const msa_problem* p, const msa_tensors* t, int32_t* selected,
+                       int32_t* page_table, float* out, void* stream) {
+  Dims d;
+  int e;
+  if ((e = check_problem(p, &d))) return e;
+  if (workspace_layout(d).total > kScratchBytes) return MSA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if ((e = hip_status(scratch_of_current_device(&ws)))) return e;
+  return decode_with_workspace(d, t, selected, page_table, out, ws, kScratchBytes,
+                               (hipStream_t)stream);
 }
 
 int msa_insert_kv(const msa_problem* p, const msa_pools* pools, const int32_t* block_table,
@@ -307,7 +368,9 @@ const char* msa_status_string(int status) {
     case MSA_OK: return "ok";
     case MSA_ERR_INVALID_ARG: return "invalid argument";
     case MSA_ERR_UNSUPPORTED: return "unsupported dtype or shape";
-    case MSA_ERR_WORKSPACE: return "workspace too small";
+    case MSA_ERR_WORKSPACE:
+      return "workspace too small (msa_decode_noalloc: the problem needs more than "
+             "MSA_NOALLOC_SCRATCH_BYTES)";
     case MSA_ERR_HIP: return "HIP launch failed";
     case MSA_ERR_BAD_DATA: return "input data failed a debug check";
     default: return "unknown status";

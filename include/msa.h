@@ -239,6 +239,25 @@ int msa_decode(const msa_problem* p, const msa_tensors* t, int32_t* selected,
                int32_t* page_table, float* out, void* workspace, size_t workspace_bytes,
                void* stream);
 
+/* Size of the per-device array msa_decode_noalloc takes its workspace from. */
+#define MSA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+/* msa_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same arguments, launches and results as msa_decode, without the
+ * workspace argument.  The workspace is a MSA_NOALLOC_SCRATCH_BYTES (16 MiB)
+ * array the library holds on each device it runs on, from the first call
+ * on that device until the process ends; problems whose
+ * msa_workspace_bytes() exceed it return MSA_ERR_WORKSPACE (the batch must
+ * be split).  The call allocates nothing.  All calls on one device share
+ * that device's array, so calls that overlap on one device (on different
+ * streams or from different host threads) race and must be serialised by
+ * the caller; the array needs no clearing between calls (every byte the
+ * kernels read was written earlier in the same call).  Runs on the current
+ * device. */
+int msa_decode_noalloc(const msa_problem* p, const msa_tensors* t, int32_t* selected,
+                       int32_t* page_table, float* out, void* stream);
+
 /* Bytes of device workspace msa_sparse_decode and msa_decode need for this
  * problem (a multiple of 256; 0 for an invalid problem).  The workspace is
  * scratch owned by the caller; its contents need no initialisation. */

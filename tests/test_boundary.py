@@ -195,3 +195,15 @@ def test_insert_arguments_are_checked_before_launch():
     # an unsupported shape is reported as such
     assert L.msa_insert_kv(ctypes.byref(good(head_dim=64)), ctypes.byref(pl), *ok,
                            None) == msa.MSA_ERR_UNSUPPORTED
+
+
+def test_noalloc_rejects_problems_beyond_its_array():
+    """msa_decode_noalloc refuses, before touching the device, a problem whose
+    workspace exceeds the library's per-device array."""
+    big = good(batch=64, max_blocks_per_seq=1 << 16, num_phys_blocks=1 << 20)
+    assert msa.msa_workspace_bytes(big) > msa.MSA_NOALLOC_SCRATCH_BYTES
+    t = msa.Tensors(*([16] * 10))
+    st = msa.lib().msa_decode_noalloc(ctypes.byref(big), ctypes.byref(t), None, None,
+                                      ctypes.c_void_p(16), None)
+    assert st == msa.MSA_ERR_WORKSPACE
+    assert "MSA_NOALLOC_SCRATCH_BYTES" in msa.msa_status_string(st)
