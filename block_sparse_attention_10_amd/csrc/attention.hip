@@ -12,9 +12,13 @@
 // Design (gfx950):
 //  * A workgroup of 4 or 8 waves owns one (row, KV head, split).  Each wave
 //    walks chunks of 32 keys (two 16-token pages) of the row's blocks; when
-//    a workgroup holds the whole row it writes the output itself.  Draft
-//    rows of one request run on one XCD, so blocks they share can be served
-//    from its L2.
+//    a workgroup holds the whole row it writes the output itself.
+//  * Multi-row requests (speculative verification, up to 4 rows) instead
+//    give one workgroup the union of the request's rows' blocks, with every
+//    (row, query head) pair as an MFMA column, so a block the rows share is
+//    read once; fp8 chunks are prefetched into LDS one chunk ahead.  Rows of
+//    longer requests keep the per-row workgroups, on one XCD per request so
+//    that blocks they share can be served from its L2.
 //  * QK^T on MFMA v_mfma_f32_16x16x32_bf16 with keys as the M dimension and
 //    the query heads of the KV head as N (one tile of 16): S^T = K Q^T; keys
 //    past the row's position are masked.  K rows go straight from HBM into
@@ -552,10 +556,443 @@ __global__ __launch_bounds__(64 * W, SEL ? 2 : 4) void sparse_attn_kernel(
   }
 }
 
+// ---- multi-row requests: one workgroup per (request, KV head, split)
+// The T rows of a speculative-verify request (news.ainew.jp article,
+// section "EAGLE3 が第 2 のデコードループを追加": flattened verify rows of one
+// request) select mostly the same blocks.  This workgroup walks the union of
+// their blocks once, with the T x G (row, query head) pairs of its KV head as
+// the MFMA columns (one or two tiles of 16), so each K/V byte of the union is
+// fetched once per request -- the reuse of key loads across draft positions
+// that section 2 of the same article gets from one indexer workgroup per
+// request.  A column masks the keys its row does not attend: blocks outside
+// the row's selection, and keys past the row's position in its local block.
+constexpr int kUnionMaxRows = 4;  // T x 16 table slots fit one wave
+
+// The union of request b's row selections, built by each wave on its own
+// from the rows' page tables (first page of each block group): on return
+// lane u < n holds union block u's physical block and its membership bits
+// (bit t: row t attends it; bit 8 + t: it is row t's local block, the last
+// group of the row).  Returns n.
+__device__ __forceinline__ int union_of_rows(const int32_t* __restrict__ page_table, int b,
+                                             int T, int PT, int lane, int& u_phys,
+                                             int& u_bits) {
+  const int t = lane >> 4, k = lane & 15;
+  int phys = -1;
+  if (t < T && 8 * k < PT) {
+    const int e = page_table[(size_t)(b * T + t) * PT + 8 * k];
+    phys = e >= 0 ? (e >> 3) : -1;
+  }
+  const uint64_t valid = __ballot(phys >= 0);
+  const int n_row = __popcll((valid >> (16 * t)) & 0xFFFFull);
+  const uint64_t localm = __ballot(phys >= 0 && k == n_row - 1);
+  // lanes holding the same block as this one
+  uint64_t same = 0;
+  for (int j = 0; j < kWave; ++j) {
+    const int pj = __builtin_amdgcn_readlane(phys, j);
+    const uint64_t m = __ballot(phys == pj);
+    if (lane == j) same = m;
+  }
+  const bool first = phys >= 0 && (same & ((1ull << lane) - 1)) == 0;
+  int bits = 0;
+#pragma unroll
+  for (int r = 0; r < kUnionMaxRows; ++r) {
+    if ((same >> (16 * r)) & 0xFFFFull) bits |= 1 << r;
+    if (((same & localm) >> (16 * r)) & 0xFFFFull) bits |= 1 << (8 + r);
+  }
+  // compact: the first lane of each block to its rank, the rest behind
+  const uint64_t firsts = __ballot(first);
+  const int n = __popcll(firsts);
+  const int below = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(firsts >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)firsts, 0u));
+  const int dst = first ? below : n + (lane - below);
+  u_phys = __builtin_amdgcn_ds_permute(dst * 4, phys);
+  u_bits = __builtin_amdgcn_ds_permute(dst * 4, bits);
+  return n;
+}
+
+// fp8 chunks are prefetched: the raw K, V and scale bytes of a wave's next
+// chunk go from HBM straight into a per-wave LDS slot (direct-to-LDS loads,
+// no registers) while the current chunk is computed, and are read back into
+// the registers load_page would have filled.  Slot layout: K loads
+// (page, half) at 1 KB each, V loads at 4 KB + 1 KB each, and 64 fp32 scales
+// (32 K scales, then 32 V scales) at 8 KB.
+constexpr int kSlotBytes = 8192 + 256;
+constexpr int kWaitLgkm = 0xC07F;  // s_waitcnt operand: lgkmcnt == 0 only
+
+// One direct-to-LDS load of 16 (or 4) bytes per lane from `src` to LDS
+// address `lds` + lane * 16 (4), non-temporal.  Written as inline asm so
+// that the compiler does not take every later LDS access of the wave as
+// dependent on it and wait for it there (it cannot tell the prefetch slot
+// from the staging area); the kernel waits for these loads itself (vmcnt)
+// before it reads the slot.  The instructions have no register outputs; m0
+// carries the LDS address.
+__device__ __forceinline__ void lds_dma_b128(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+               :
+               : "v"(src), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma_b32(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off nt"
+               :
+               : "v"(src), "s"(lds)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_address(const uint8_t* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+
+__device__ __forceinline__ void prefetch_chunk_fp8(uint8_t* slot,
+                                                   const uint8_t* __restrict__ k_pool,
+                                                   const uint8_t* __restrict__ v_pool,
+                                                   const float* __restrict__ k_scale,
+                                                   const float* __restrict__ v_scale,
+                                                   size_t row0, int lane) {
+  const int m = lane & 15, g = lane >> 4;
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_address(slot));
+#pragma unroll
+  for (int jp = 0; jp < 2; ++jp) {
+    const size_t r = row0 + 16 * jp;
+    const uint8_t* kp = k_pool + (r + m) * 128 + 16 * g;
+    const uint8_t* vp = v_pool + r * 128 + 16 * lane;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      lds_dma_b128(kp + 64 * i, base + (2 * jp + i) * 1024);
+      lds_dma_b128(vp + 1024 * i, base + 4096 + (2 * jp + i) * 1024);
+    }
+  }
+  const float* sp = (lane < 32 ? k_scale : v_scale) + row0 + (lane & 31);
+  lds_dma_b32(sp, base + 8192);
+}
+
+// The registers of page jp of a prefetched fp8 chunk, as load_page<1> fills
+// them.
+__device__ __forceinline__ void read_page_fp8(Chunk<1>& c, const uint8_t* slot, int jp,
+                                              int lane) {
+  const int g = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    c.k[i] = *reinterpret_cast<const u32x4*>(slot + (2 * jp + i) * 1024 + 16 * lane);
+    c.v[i] = *reinterpret_cast<const u32x4*>(slot + 4096 + (2 * jp + i) * 1024 + 16 * lane);
+  }
+  c.kscale = *reinterpret_cast<const f32x4*>(slot + 8192 + (16 * jp + 4 * g) * 4);
+  c.vscale = *reinterpret_cast<const f32x4*>(slot + 8192 + 128 + (16 * jp + 4 * g) * 4);
+}
+
+// s_waitcnt operand that waits until at most n vector-memory operations
+// are outstanding (gfx9 encoding: vmcnt bits [3:0] and [15:14]).
+constexpr int vmcnt_imm(int n) { return ((n >> 4) << 14) | 0x0F70 | (n & 15); }
+constexpr int kDmaPerChunk = 9;  // direct-to-LDS loads per prefetched fp8 chunk
+
+// Every wave computes all NT tiles of each of its chunks, so each union
+// block is loaded once per request.  fp8 (D > 0): each wave keeps up to D
+// chunks in flight in a ring of LDS slots.
+template <int KV, int W, int NT, int D>
+__global__ __launch_bounds__(64 * W, W == 4 ? 1 : 2) void union_attn_kernel(
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ k_pool,
+    const uint8_t* __restrict__ v_pool, const void* __restrict__ k_scale,
+    const void* __restrict__ v_scale, const int32_t* __restrict__ page_table,
+    const int32_t* __restrict__ ctx_lens, float* __restrict__ part_o,
+    float* __restrict__ part_ml, float* __restrict__ out, int B, int T, int Hq, int Hkv, int PT,
+    int S, int max_block, float scale_log2) {
+  constexpr bool kPrefetch = D > 0;
+  static_assert(!kPrefetch || KV == 1, "prefetch ring for fp8 chunks");
+  static_assert(D <= 3, "vmcnt waits below cover up to 3 chunks in flight");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[W * kWaveLds];
+  __shared__ __attribute__((aligned(16))) uint8_t slots[kPrefetch ? W * D * kSlotBytes : 16];
+
+  const int lane = lane_id();
+  const int wave = wave_id();
+  int x = blockIdx.x;
+  const int split = x % S;
+  x /= S;
+  const int g = x % Hkv;
+  const int b = x / Hkv;
+  if (b >= B) return;
+  const int G = Hq / Hkv;
+  const int L = ctx_lens[b];
+
+  // Column hl of tile j is (row t, query head h) = divmod(16 j + hl, G);
+  // Q^T operands as in the per-row kernel, zero for columns past T G.
+  const int hl = lane & 15;
+  const int g4 = lane >> 4;
+  bf16x8 qop[NT][4];
+  int trow[NT], vloc[NT];
+  bool cvalid[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const int col = 16 * j + hl;
+    cvalid[j] = col < T * G;
+    const int cc = cvalid[j] ? col : 0;
+    trow[j] = cc / G;
+    vloc[j] = ((L - T + trow[j]) & 127) + 1;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const uint16_t* qp = q + ((size_t)(b * T + trow[j]) * Hq + g * G + cc % G) * kD;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const u32x4 v = ldg128(qp + kdim<KV>(g4, kk));
+      qop[j][kk] = __builtin_bit_cast(bf16x8, cvalid[j] ? v : z);
+    }
+  }
+
+  // rows whose columns fall in tile j: a chunk of a block none of them
+  // selects skips the tile's work (its columns would all be masked)
+  int tmask[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    tmask[j] = 0;
+    for (int r = 0; r < T; ++r)
+      if (r * G < 16 * j + 16 && (r + 1) * G > 16 * j) tmask[j] |= 1 << r;
+  }
+
+  int u_phys, u_bits;
+  const int nU = union_of_rows(page_table, b, T, PT, lane, u_phys, u_bits);
+  const int nchunks = 4 * nU;
+
+  float m[NT], lsum[NT];
+  f32x4 oacc[NT][8];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    m[j] = neg_inf();
+    lsum[j] = 0.f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) oacc[j][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  uint8_t* stage = smem + wave * kWaveLds;
+  uint8_t* ring = slots + (kPrefetch ? wave * D * kSlotBytes : 0);
+  // Keys of union block u that some row attends: all of it when it is not
+  // the local block of every row that selects it, else up to the position
+  // of the last such row (positions rise with t inside one block).  A chunk
+  // wholly past that is skipped.
+  auto wanted = [&](int ci) {
+    const int bits = __builtin_amdgcn_readlane(u_bits, ci >> 2);
+    const int rows = bits & 0xFF, locs = (bits >> 8) & 0xFF;
+    const int reach = (rows & ~locs) ? 128 : ((L - T + (31 - __builtin_clz(locs))) & 127) + 1;
+    return (ci & 3) * 32 < reach;
+  };
+  auto next_wanted = [&](int ci) {
+    while (ci < nchunks && !wanted(ci)) ci += S * W;
+    return ci;
+  };
+  auto chunk_row0 = [&](int ci) {
+    const int P = __builtin_amdgcn_readlane(u_phys, ci >> 2);
+    const int phys = min(max(P, 0), max_block);  // a bad table cannot leave the pools
+    return ((size_t)phys * Hkv + g) * 128 + (size_t)(ci & 3) * 32;
+  };
+
+  int ci = next_wanted(split + S * wave);
+  // the ring: chunks are consumed in the order they were issued; `ahead`
+  // is the next chunk to issue, `inflight` how many sit in the ring
+  int ahead = ci, inflight = 0, cur = 0;
+  auto issue = [&](int sl) {
+    prefetch_chunk_fp8(ring + sl * kSlotBytes, k_pool, v_pool,
+                       static_cast<const float*>(k_scale), static_cast<const float*>(v_scale),
+                       chunk_row0(ahead), lane);
+    ahead = next_wanted(ahead + S * W);
+    ++inflight;
+  };
+  if constexpr (kPrefetch) {
+    for (int sl = 0; sl < D && ahead < nchunks; ++sl) issue(sl);
+  }
+  while (ci < nchunks) {
+    const int bits = __builtin_amdgcn_readlane(u_bits, ci >> 2);
+    const int pg0 = (ci & 3) * 2;
+    const size_t row0 = chunk_row0(ci);
+    const int nci = next_wanted(ci + S * W);
+    Chunk<KV> ch[2];
+    if constexpr (kPrefetch) {
+      // this chunk (the oldest in flight) has landed once no more than the
+      // younger chunks' loads are outstanding
+      if (inflight >= 3)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kDmaPerChunk));
+      else if (inflight == 2)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kDmaPerChunk));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      asm volatile("" ::: "memory");
+      uint8_t* slot = ring + cur * kSlotBytes;
+#pragma unroll
+      for (int jp = 0; jp < 2; ++jp) read_page_fp8(ch[jp], slot, jp, lane);
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm);  // slot read: it may take the next chunk
+      asm volatile("" ::: "memory");
+      --inflight;
+      if (ahead < nchunks) issue(cur);
+      cur = cur + 1 == D ? 0 : cur + 1;
+    } else {
+#pragma unroll
+      for (int jp = 0; jp < 2; ++jp)
+        load_page<KV>(ch[jp], k_pool, v_pool, k_scale, v_scale, row0 + 16 * jp, lane);
+    }
+    if constexpr (KV == 0) {
+#pragma unroll
+      for (int jp = 0; jp < 2; ++jp)
+        load_v_lds(v_pool, row0 + 16 * jp, lane, stage + 16 * jp * kVRow);
+    } else {
+#pragma unroll
+      for (int jp = 0; jp < 2; ++jp) stage_v<KV>(ch[jp], stage + 16 * jp * kVRow, lane);
+    }
+
+    bf16x8 phi[NT], plo[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      if (!(bits & tmask[j])) continue;
+      // S^T = K Q^T for the two pages, this tile's columns
+      f32x4 sacc[2];
+#pragma unroll
+      for (int jp = 0; jp < 2; ++jp) {
+        sacc[jp] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          sacc[jp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<KV>(ch[jp], kk),
+                                                             qop[j][kk], sacc[jp], 0, 0, 0);
+      }
+      // this column's keys: none when its row does not select the block, up
+      // to its position when the block is its row's local block
+      const bool inrow = cvalid[j] && ((bits >> trow[j]) & 1);
+      const bool isloc = (bits >> (8 + trow[j])) & 1;
+      const int lim = inrow ? (isloc ? vloc[j] : 128) : 0;
+      float z[8];
+      float mc = neg_inf();
+#pragma unroll
+      for (int jp = 0; jp < 2; ++jp)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float v = sacc[jp][i] * scale_log2;
+          if constexpr (KV == 1) v *= ch[jp].kscale[i];
+          const int tok = 16 * (pg0 + jp) + 4 * g4 + i;
+          v = tok < lim ? v : neg_inf();
+          z[4 * jp + i] = v;
+          mc = fmaxf(mc, v);
+        }
+      mc = fmaxf(mc, __shfl_xor(mc, 16));
+      mc = fmaxf(mc, __shfl_xor(mc, 32));
+      const float mn = fmaxf(m[j], mc);
+      const float alpha = mn == m[j] ? 1.f : __builtin_amdgcn_exp2f(m[j] - mn);
+      m[j] = mn;
+      // P as bf16 hi + lo (two values per conversion), V scales folded in
+      float psum = 0.f;
+      float pv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pe = z[e] == neg_inf() ? 0.f : __builtin_amdgcn_exp2f(z[e] - mn);
+        psum += pe;
+        pv[e] = pe;
+        if constexpr (KV == 1) pv[e] *= ch[e >> 2].vscale[e & 3];
+      }
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const f32x2 pp = {pv[2 * w], pv[2 * w + 1]};
+        hw[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pp, bf16x2));
+        const f32x2 rest = {pp.x - bf16_bits_to_f32(hw[w] & 0xFFFFu),
+                            pp.y - __builtin_bit_cast(float, hw[w] & 0xFFFF0000u)};
+        lw[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(rest, bf16x2));
+      }
+      phi[j] = __builtin_bit_cast(bf16x8, (u32x4{hw[0], hw[1], hw[2], hw[3]}));
+      plo[j] = __builtin_bit_cast(bf16x8, (u32x4{lw[0], lw[1], lw[2], lw[3]}));
+      lsum[j] = lsum[j] * alpha + psum;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) oacc[j][s] *= alpha;
+    }
+
+    if constexpr (KV == 0) __builtin_amdgcn_s_waitcnt(kWaitVmem);  // V rows landed in LDS
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // O^T += V^T P^T per tile; the V^T operand is shared by the tiles
+    const int vrow = 4 * g4 + (hl >> 2);
+    const uint8_t* vrd = stage + vrow * kVRow + 8 * (hl & 3);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      bf16x8 aop;
+      if constexpr (KV == 0) {
+        const uint8_t* colp = stage + 32 * (s ^ g4) + 2 * hl;
+        uint32_t a[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t x0 = *reinterpret_cast<const uint16_t*>(colp + kappa(g4, 2 * w) * kVRow);
+          const uint32_t x1 =
+              *reinterpret_cast<const uint16_t*>(colp + kappa(g4, 2 * w + 1) * kVRow);
+          a[w] = x0 | (x1 << 16);
+        }
+        const u32x4 av = {a[0], a[1], a[2], a[3]};
+        aop = __builtin_bit_cast(bf16x8, av);
+      } else {
+        const uint8_t* p0 = vrd + 32 * (s ^ (vrow & 7));
+        const v4i16 k0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p0);
+        const v4i16 k1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p0 + 16 * kVRow));
+        const v8i16 kv = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+        aop = __builtin_bit_cast(bf16x8, kv);
+      }
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        if (!(bits & tmask[j])) continue;
+        oacc[j][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, phi[j], oacc[j][s], 0, 0, 0);
+        oacc[j][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, plo[j], oacc[j][s], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    ci = nci;
+  }
+
+  // ---- combine the W waves in LDS, one tile at a time
+  float* m_w = reinterpret_cast<float*>(smem);  // [W][16]
+  float* l_w = m_w + 16 * W;                    // [W][16]
+  float* o_w = l_w + 16 * W;                    // [W][16][kORow]
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    float ls = lsum[j];
+    ls += __shfl_xor(ls, 16);
+    ls += __shfl_xor(ls, 32);
+    __syncthreads();
+    if (lane < 16) {
+      m_w[wave * 16 + lane] = m[j];
+      l_w[wave * 16 + lane] = ls;
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        o_w[(wave * 16 + hl) * kORow + 16 * s + 4 * g4 + i] = oacc[j][s][i];
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < 16 * kD; idx += 64 * W) {
+      const int c = idx >> 7;
+      const int d = idx & (kD - 1);
+      const int col = 16 * j + c;
+      if (col >= T * G) break;  // idx rises with c
+      float M = neg_inf();
+#pragma unroll
+      for (int w = 0; w < W; ++w) M = fmaxf(M, m_w[w * 16 + c]);
+      float O = 0.f, Ls = 0.f;
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        const float mw = m_w[w * 16 + c];
+        const float f = mw == neg_inf() ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+        O += f * o_w[(w * 16 + c) * kORow + d];
+        Ls += f * l_w[w * 16 + c];
+      }
+      const size_t rh = (size_t)(b * T + col / G) * Hq + g * G + col % G;
+      if (S == 1) {
+        out[rh * kD + d] = Ls > 0.f ? O / Ls : 0.f;
+      } else {
+        part_o[(rh * S + split) * kD + d] = O;
+        if (d == 0) {
+          part_ml[(rh * S + split) * 2] = M;
+          part_ml[(rh * S + split) * 2 + 1] = Ls;
+        }
+      }
+    }
+  }
+}
+
 // out[rh][d] = sum_s 2^(m_s - M) O_s[d] / sum_s 2^(m_s - M) l_s
-// Splits per row never exceed kMaxSplits (at most 64 chunks of 32 keys per
-// row, at least 8 per split); every split's (m, l) and partial row load in
-// one round trip, then combine in split order.
+// Splits per row never exceed kMaxSplits (plan_splits caps them); every
+// split's (m, l) and partial row load in one round trip, then combine in
+// split order.
 constexpr int kMaxSplits = 8;
 
 __global__ __launch_bounds__(128) void lse_merge_kernel(const float* __restrict__ part_o,
@@ -608,8 +1045,36 @@ __global__ void selftest_kernel(float* out) {
 // Workgroups of one launch; with T > 1 the request count is padded to a
 // multiple of 8 for the XCD-aware id mapping.
 long attention_workgroups(const Dims& d, const SplitPlan& sp) {
+  if (sp.rows_union) return (long)d.B * d.Hkv * sp.splits;
   const long reqs = d.T > 1 ? (d.B + 7) / 8 * 8 : d.B;
   return reqs * d.T * d.Hkv * sp.splits;
+}
+
+// fp8 union workgroups: 8 waves, each with its next chunk in flight in an
+// LDS slot while it computes the current one (one workgroup per CU: 135 KB
+// of LDS, about 215 registers); other formats: 8 waves, no prefetch.
+// Measured on MI355X (fp8 spec-verify layer, 128 requests x 4 rows, step
+// after a 1 GiB cache flush / back to back): 81.5 / 77.8 us, against 90.9 /
+// 74.5 us for one workgroup per row; 4 waves with 3 chunks in flight each
+// took 97.4 / 92.7 us (one wave per SIMD leaves the per-chunk compute
+// exposed).
+constexpr int kUnionWavesFp8 = 8;
+constexpr int kUnionDepthFp8 = 1;
+
+template <int KV, int NT>
+hipError_t launch_union(const Dims& d, const SplitPlan& sp, const void* q, const void* k_pool,
+                        const void* v_pool, const void* k_scale, const void* v_scale,
+                        const int32_t* page_table, const int32_t* ctx_lens, float* part_o,
+                        float* part_ml, float* out, hipStream_t s) {
+  constexpr int W = KV == 1 ? kUnionWavesFp8 : 8;
+  constexpr int D = KV == 1 ? kUnionDepthFp8 : 0;
+  hipLaunchKernelGGL((union_attn_kernel<KV, W, NT, D>),
+                     dim3((unsigned)attention_workgroups(d, sp)), dim3(64 * W), 0, s,
+                     static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(k_pool),
+                     static_cast<const uint8_t*>(v_pool), k_scale, v_scale, page_table,
+                     ctx_lens, part_o, part_ml, out, d.B, d.T, d.Hq, d.Hkv, d.PT(), sp.splits,
+                     d.NB - 1, d.scale_log2);
+  return hipGetLastError();
 }
 
 template <int KV, int W, bool SEL>
@@ -631,6 +1096,13 @@ hipError_t launch_kv(const Dims& d, const SplitPlan& sp, const void* q, const vo
                      const void* v_pool, const void* k_scale, const void* v_scale,
                      const int32_t* page_table, const int32_t* ctx_lens, float* part_o,
                      float* part_ml, float* out, const SelectArgs* sel, hipStream_t s) {
+  if (sp.rows_union) {
+    if (sp.tiles == 1)
+      return launch_union<KV, 1>(d, sp, q, k_pool, v_pool, k_scale, v_scale, page_table,
+                                 ctx_lens, part_o, part_ml, out, s);
+    return launch_union<KV, 2>(d, sp, q, k_pool, v_pool, k_scale, v_scale, page_table,
+                               ctx_lens, part_o, part_ml, out, s);
+  }
   if (sel)
     return launch_kvw<KV, 8, true>(d, sp, q, k_pool, v_pool, k_scale, v_scale, nullptr,
                                    ctx_lens, part_o, part_ml, out, *sel, s);
@@ -644,18 +1116,34 @@ hipError_t launch_kv(const Dims& d, const SplitPlan& sp, const void* q, const vo
 
 }  // namespace
 
+// Multi-row requests with at most this many rows walk the union of their
+// rows' blocks in one workgroup (the rows' table slots fit one wave), when
+// their (row, query head) pairs fit two 16-column tiles.
+bool union_eligible(const Dims& d) {
+  return d.T > 1 && d.T <= kUnionMaxRows && d.T * d.G() <= 32;
+}
+
 SplitPlan plan_splits(const Dims& d) {
-  // One workgroup per (row, KV head, split).  Rows are split only until
-  // there is one workgroup per CU (256), keeping at least one chunk of 32
-  // keys per wave of 8.  On MI355X 8 waves per workgroup measured faster
-  // than 4 or 16, and fewer splits faster than more (less merging).
+  // One workgroup per (row, KV head, split), or per (request, KV head,
+  // split) for multi-row requests that walk their union.  Work is split
+  // only until there is one workgroup per CU (256), keeping at least one
+  // chunk of 32 keys per wave of 8.  On MI355X 8 waves per workgroup
+  // measured faster than 4 or 16, and fewer splits faster than more (less
+  // merging).
   SplitPlan p;
-  const int chunks = 4 * d.topk;  // at most 4 chunks per selected block
-  const long pairs = (long)d.R() * d.Hkv;
+  p.rows_union = union_eligible(d);
+  p.tiles = p.rows_union ? (d.T * d.G() + 15) / 16 : 1;
+  // at most 4 chunks per selected block (of the union: T times the rows')
+  const int chunks = 4 * d.topk * (p.rows_union ? d.T : 1);
+  const long pairs = p.rows_union ? (long)d.B * d.Hkv : (long)d.R() * d.Hkv;
+  const long target = 256;
   int S = 1;
-  while (S * 2 <= chunks / 8 && pairs * S < 256) S *= 2;
+  while (S * 2 <= chunks / 8 && S * 2 <= kMaxSplits && pairs * S < target) S *= 2;
   p.splits = S;
-  p.waves = (chunks + S - 1) / S >= 8 ? 8 : 4;
+  if (p.rows_union)
+    p.waves = d.kv_dtype == 1 ? kUnionWavesFp8 : 8;
+  else
+    p.waves = (chunks + S - 1) / S >= 8 ? 8 : 4;
   return p;
 }
 
@@ -690,7 +1178,8 @@ hipError_t launch_sparse_attention(const Dims& d, const void* q, const void* k_p
   if (e != hipSuccess) return e;
   static const char* names[3] = {"bf16", "fp8", "nvfp4"};
   if (note)
-    *note += std::string("sparse_attn<") + names[d.kv_dtype] + ">" +
+    *note += std::string(sp.rows_union ? "sparse_attn_union<" : "sparse_attn<") +
+             names[d.kv_dtype] + ">" +
              (sel ? "+select_topk" : "") + "[grid=" +
              std::to_string(attention_workgroups(d, sp)) + "x" + std::to_string(64 * sp.waves) +
              ",splits=" + std::to_string(sp.splits) + "]";

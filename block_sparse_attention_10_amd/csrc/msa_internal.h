@@ -26,7 +26,11 @@ struct Dims {
 // the `splits` workgroups of a (row, KV head) share its chunks of 32 keys.
 struct SplitPlan {
   int waves;   // waves per workgroup: 4 or 8
-  int splits;  // workgroups per (row, KV head)
+  int splits;  // workgroups per (row, KV head), or per (request, KV head) with rows_union
+  // multi-row requests: one workgroup walks the union of the request's rows'
+  // blocks for all of them (rows x query heads of the KV head as columns)
+  bool rows_union;
+  int tiles;   // 16-column MFMA tiles of a rows_union workgroup (1 or 2)
 };
 SplitPlan plan_splits(const Dims& d);
 

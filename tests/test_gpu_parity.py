@@ -200,6 +200,38 @@ def test_workspace_too_small_is_rejected():
     assert ei.value.status == msa.MSA_ERR_WORKSPACE
 
 
+@pytest.mark.parametrize("kw,union", [
+    (dict(batch=3, query_len=4, ctx_lo=3000, ctx_hi=12000, kv_dtype="fp8", idx_dtype="fp8",
+          seed=51), True),
+    (dict(batch=2, query_len=2, ctx_lo=2100, ctx_hi=9000, num_q_heads=16, num_kv_heads=1,
+          num_idx_heads=2, seed=52), True),
+    (dict(batch=3, query_len=3, ctx_lo=3, ctx_hi=6000, num_q_heads=20, num_kv_heads=2,
+          kv_dtype="nvfp4", idx_dtype="fp8", seed=53), True),
+    (dict(batch=2, query_len=4, ctx_list=(4, 2051), num_q_heads=4, num_kv_heads=1, topk=3,
+          seed=54), True),
+    (dict(batch=2, query_len=3, ctx_lo=3000, ctx_hi=9000, num_q_heads=16, num_kv_heads=1,
+          seed=55), False),
+    (dict(batch=2, query_len=5, ctx_lo=3000, ctx_hi=9000, kv_dtype="fp8", idx_dtype="fp8",
+          seed=56), False),
+], ids=["T4G8-fp8", "T2G16", "T3G10-nvfp4", "T4G4-topk3", "T3G16-rows", "T5G8-rows"])
+def test_multi_row_union_attention(kw, union):
+    """Multi-row requests whose (row, query head) pairs fit two 16-column
+    tiles (T <= 4) walk the union of their rows' blocks in one workgroup;
+    the others keep one workgroup per row.  Both match the oracle."""
+    cfg = small_config(**kw)
+    _say(f"multi-row attention {kw}")
+    w = make_workload(cfg, DEV)
+    rows = list(range(cfg.rows))
+    got = run_stages(w)
+    rec = msa.msa_last_dispatch()
+    assert ("sparse_attn_union<" in rec) == union, rec
+    err = compare_rows(w, got, rows)
+    fused = run_fused(w)
+    for k in ("selected", "page_table", "out"):
+        assert torch.equal(fused[k], got[k]), f"fused {k} differs from stage-wise"
+    _say(f"  max abs err {err:.3g} (tol {TOL[cfg.kv_dtype]})")
+
+
 # --------------------------------------------------------- full workloads
 @pytest.mark.parametrize("name", CONFIG_ORDER + EXTRA_CONFIGS)
 def test_full_workload_parity(name):
