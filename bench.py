@@ -7,8 +7,11 @@ layer: 64 requests with contexts uniform in [8192, 131072], 64 query / 4 KV /
 4 index heads, bf16 KV and index keys.
 
 Prints one JSON line: query-tokens/s for the whole batch, the roofline of
-the dominant kernel (the index-key scan) measured live with HIP events, and
-the CPU oracle timed on a bounded sample of the same workload.
+the dominant kernel (the index-key scan) measured live with HIP events, the
+CPU oracle timed on the same workload (median of 3 passes on all host
+cores, plus single-core runs on the two smallest configurations), and a
+compact record per other configuration (step time back to back and after a
+cache flush, end-to-end and scan fractions of the HBM peak).
 
     python bench.py [--steps K] [--warmup W] [--workload layer_128k]
 """
@@ -86,10 +89,11 @@ def measured_traffic(workload):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, n_requests, min_seconds=10.0):
+def cpu_baseline(w, n_requests, passes=3, threads=None):
     """The oracle on `n_requests` requests of the workload (their rows only):
-    scan, selection, page table and attention, timed on the host cores and
-    repeated until at least `min_seconds` of oracle time have passed."""
+    scan, selection, page table and attention, `passes` times on the host
+    cores (`threads` worker threads, default all), reporting the median
+    pass.  Gathering the compact host pools is not timed."""
     import numpy as np
     import torch
 
@@ -107,7 +111,7 @@ def cpu_baseline(w, n_requests, min_seconds=10.0):
             return x.view(torch.int16).numpy().view(np.uint16)
         return x.numpy()
 
-    # compact index-key pool of the sampled requests (gathering is not timed)
+    # compact index-key pool of the sampled requests
     nblk = [w.nblk[b] for b in reqs]
     maxb = max(nblk)
     bt = np.zeros((len(reqs), maxb), dtype=np.int32)
@@ -144,26 +148,32 @@ def cpu_baseline(w, n_requests, min_seconds=10.0):
               for k in ("k_pool", "v_pool", "k_scale", "v_scale")}
         return kv, bt_kv
 
-    elapsed, passes, kv = 0.0, 0, None
-    while passes == 0 or elapsed < min_seconds:
-        t0 = time.perf_counter()
-        s = oracle.index_scores(P, iq, ik, bt, ctx, idx_k_scale=iks)
-        sel, _ = oracle.select(P, s, ctx)
-        oracle.page_table(P, sel, bt)
-        t1 = time.perf_counter()
-        if kv is None:
-            kv, bt_kv = kv_of_selected(sel)
-        t2 = time.perf_counter()
-        oracle.attention(P, q, kv["k_pool"], kv["v_pool"], kv["k_scale"], kv["v_scale"], bt_kv,
-                         ctx, sel)
-        elapsed += (t1 - t0) + (time.perf_counter() - t2)
-        passes += 1
+    all_threads = oracle.num_threads()
+    if threads is not None:
+        oracle.set_num_threads(threads)
+    try:
+        used = oracle.num_threads()
+        times, kv = [], None
+        for _ in range(passes):
+            t0 = time.perf_counter()
+            s = oracle.index_scores(P, iq, ik, bt, ctx, idx_k_scale=iks)
+            sel, _ = oracle.select(P, s, ctx)
+            oracle.page_table(P, sel, bt)
+            t1 = time.perf_counter()
+            if kv is None:
+                kv, bt_kv = kv_of_selected(sel)
+            t2 = time.perf_counter()
+            oracle.attention(P, q, kv["k_pool"], kv["v_pool"], kv["k_scale"], kv["v_scale"],
+                             bt_kv, ctx, sel)
+            times.append((t1 - t0) + (time.perf_counter() - t2))
+    finally:
+        oracle.set_num_threads(all_threads)
     rows = len(reqs) * T
-    return {"value": rows * passes / elapsed, "unit": "query-tokens/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
+    med = sorted(times)[len(times) // 2]
+    return {"value": rows / med, "unit": "query-tokens/s", "cores": used, "kind": "oracle",
             "sample": f"{len(reqs)} of {c.batch} requests ({rows} query rows, full contexts), "
-                      f"{passes} passes, {elapsed:.1f} s",
-            "cpu": cpu_model(), "host_cpus": os.cpu_count()}
+                      f"median of {passes} passes",
+            "pass_s": [round(x, 4) for x in times]}
 
 
 def cpu_model():
@@ -177,6 +187,121 @@ def cpu_model():
     return None
 
 
+def describe_workload(cfg):
+    return (f"{cfg.name}: batch {cfg.batch}, decode_query_len {cfg.query_len}, "
+            f"context U[{cfg.ctx_lo}, {cfg.ctx_hi}], heads q/kv/idx "
+            f"{cfg.num_q_heads}/{cfg.num_kv_heads}/{cfg.num_idx_heads}, "
+            f"KV {cfg.kv_dtype}, index keys {cfg.idx_dtype}, top-{cfg.topk} "
+            f"blocks of 128 with the local block")
+
+
+class Timed:
+    """One workload resident on the GPU with its descriptor and buffers."""
+
+    def __init__(self, cfg):
+        import torch
+
+        import block_sparse_attention_10_amd as msa
+        from synth import make_workload
+
+        self.msa = msa
+        self.cfg = cfg
+        self.w = make_workload(cfg, "cuda")
+        torch.cuda.synchronize()
+        wt = self.w.tensors
+        self.p, self.t = msa.describe(wt["q"], wt["idx_q"], wt["k_pool"], wt["v_pool"],
+                                      wt["k_scale"], wt["v_scale"], wt["idx_k_pool"],
+                                      wt["block_table"], wt["ctx_lens"],
+                                      decode_query_len=cfg.query_len, topk=cfg.topk,
+                                      idx_k_scale=wt.get("idx_k_scale"))
+        R = cfg.rows
+        self.scores = torch.empty((R, cfg.max_blocks), dtype=torch.float32, device="cuda")
+        self.selected = torch.empty((R, cfg.topk), dtype=torch.int32, device="cuda")
+        self.out = torch.empty((R, cfg.num_q_heads, 128), dtype=torch.float32, device="cuda")
+        self.ws = torch.empty((msa.msa_workspace_bytes(self.p),), dtype=torch.uint8,
+                              device="cuda")
+        msa.msa_decode(self.p, self.t, self.selected, None, self.out, self.ws)
+        torch.cuda.synchronize()
+        self.ab = algorithmic_bytes(self.w, self.selected.cpu().numpy())
+
+    def step(self):
+        self.msa.msa_decode(self.p, self.t, None, None, self.out, self.ws)
+
+    def scan(self):
+        self.msa.msa_index_score(self.p, self.t, self.scores)
+
+
+def time_loop(fn, steps, warmup):
+    """Mean microseconds per call of `fn`, back to back on the current stream,
+    measured with HIP events on that stream."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps * 1e3
+
+
+def time_cold(fn, steps):
+    """Percentiles of single calls, each after a 1 GiB write that evicts the
+    L2s and the 256 MB last-level cache (the write is outside the events)."""
+    import torch
+
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    cold = []
+    for _ in range(steps):
+        flush.fill_(1.0)
+        start.record()
+        fn()
+        end.record()
+        torch.cuda.synchronize()
+        cold.append(start.elapsed_time(end) * 1e3)
+    del flush
+    cold.sort()
+    return {"p10": cold[len(cold) // 10], "p50": cold[len(cold) // 2],
+            "p90": cold[(9 * len(cold)) // 10], "steps": len(cold)}
+
+
+def workload_record(cfg, steps, warmup, cold_steps):
+    """Step time (back to back and after a cache flush), the end-to-end
+    fraction of the HBM peak and the scan's own fraction, for one workload."""
+    import torch
+
+    tw = Timed(cfg)
+    warm_us = time_loop(tw.step, steps, warmup)
+    cold = time_cold(tw.step, cold_steps)
+    dispatch = tw.msa.msa_last_dispatch()
+    scan_us = time_loop(tw.scan, steps, warmup)
+    ab = tw.ab
+    rec = {
+        "workload": describe_workload(cfg),
+        "rows": cfg.rows,
+        "step_us": round(warm_us, 2),
+        "step_us_after_cache_flush_p50": round(cold["p50"], 2),
+        "query_tokens_per_s": cfg.rows / (warm_us * 1e-6),
+        "query_tokens_per_s_after_cache_flush": cfg.rows / (cold["p50"] * 1e-6),
+        "algorithmic_bytes_per_step": ab["total"],
+        "frac_of_peak_end_to_end": ab["total"] / (warm_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+        "frac_of_peak_end_to_end_after_cache_flush":
+            ab["total"] / (cold["p50"] * 1e-6) / 1e9 / PEAK_HBM_GBS,
+        "scan_us": round(scan_us, 2),
+        "scan_frac_of_peak": ab["index"] / (scan_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+        "kernels": dispatch,
+    }
+    del tw
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -184,8 +309,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="layer_128k")
     ap.add_argument("--cpu-requests", type=int, default=64,
-                    help="requests the CPU oracle baseline runs on")
+                    help="requests the all-core CPU oracle baseline runs on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the per-workload records of the other configurations")
     ap.add_argument("--export-spec", default=None,
                     help="write the workload's shapes, contexts and block table for the "
                          "counter driver (msa_counters.cpp) and exit")
@@ -204,87 +331,32 @@ def main():
 
     import torch
 
-    import block_sparse_attention_10_amd as msa
-    from synth import CONFIGS, make_workload
+    from synth import CONFIG_ORDER, CONFIGS, EXTRA_CONFIGS
 
     cfg = CONFIGS[args.workload]
-    w = make_workload(cfg, "cuda")
-    torch.cuda.synchronize()
+    tw = Timed(cfg)
+    msa = tw.msa
+    w, p, t, o_out, ws = tw.w, tw.p, tw.t, tw.out, tw.ws
     wt = w.tensors
-    p, t = msa.describe(wt["q"], wt["idx_q"], wt["k_pool"], wt["v_pool"], wt["k_scale"],
-                        wt["v_scale"], wt["idx_k_pool"], wt["block_table"], wt["ctx_lens"],
-                        decode_query_len=cfg.query_len, topk=cfg.topk,
-                        idx_k_scale=wt.get("idx_k_scale"))
     R = cfg.rows
-    o = {
-        "scores": torch.empty((R, cfg.max_blocks), dtype=torch.float32, device="cuda"),
-        "selected": torch.empty((R, cfg.topk), dtype=torch.int32, device="cuda"),
-        "out": torch.empty((R, cfg.num_q_heads, 128), dtype=torch.float32, device="cuda"),
-        "workspace": torch.empty((msa.msa_workspace_bytes(p),), dtype=torch.uint8,
-                                 device="cuda"),
-    }
-    msa.msa_decode(p, t, o["selected"], None, o["out"], o["workspace"])
-    torch.cuda.synchronize()
-    ab = algorithmic_bytes(w, o["selected"].cpu().numpy())
+    ab = tw.ab
 
-    def step():
-        msa.msa_decode(p, t, None, None, o["out"], o["workspace"])
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(args.steps):
-        step()
-    end.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
+    us = time_loop(tw.step, args.steps, args.warmup)
+    ms = us * 1e-3
     dispatch = msa.msa_last_dispatch()
-
-    # cold-cache steps: each timed alone after a 1 GiB write that evicts the
-    # L2s and the 256 MB last-level cache (the flush is outside the events)
-    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
-    cold = []
-    for _ in range(min(args.steps, 20)):
-        flush.fill_(1.0)
-        start.record()
-        step()
-        end.record()
-        torch.cuda.synchronize()
-        cold.append(start.elapsed_time(end) * 1e3)
-    del flush
-    cold.sort()
-    cold_us = {"p10": cold[len(cold) // 10], "p50": cold[len(cold) // 2],
-               "p90": cold[(9 * len(cold)) // 10], "steps": len(cold)}
+    cold_us = time_cold(tw.step, min(args.steps, 20))
 
     # the dominant kernel alone: index-key scan, same stream, same buffers
-    for _ in range(args.warmup):
-        msa.msa_index_score(p, t, o["scores"])
-    torch.cuda.synchronize()
-    start.record()
-    for _ in range(args.steps):
-        msa.msa_index_score(p, t, o["scores"])
-    end.record()
-    torch.cuda.synchronize()
-    scan_us = start.elapsed_time(end) / args.steps * 1e3
+    scan_us = time_loop(tw.scan, args.steps, args.warmup)
     achieved = ab["index"] / (scan_us * 1e-6) / 1e9
 
     # a layer that reuses another layer's selection (index sharing across
     # adjacent sparse layers): attention over a page table, scan and
     # selection skipped
     pt = torch.empty((R, cfg.topk * 8), dtype=torch.int32, device="cuda")
-    msa.msa_decode(p, t, None, pt, o["out"], o["workspace"])
-    for _ in range(args.warmup):
-        msa.msa_sparse_decode(p, t, pt, o["out"], o["workspace"])
-    torch.cuda.synchronize()
-    start.record()
-    for _ in range(args.steps):
-        msa.msa_sparse_decode(p, t, pt, o["out"], o["workspace"])
-    end.record()
-    torch.cuda.synchronize()
-    reuse_us = start.elapsed_time(end) / args.steps * 1e3
+    msa.msa_decode(p, t, None, pt, o_out, ws)
+    reuse_us = time_loop(lambda: msa.msa_sparse_decode(p, t, pt, o_out, ws), args.steps,
+                         args.warmup)
 
     # the write path of a step: the R new tokens' K, V and index keys go into
     # the pools (quantised to their formats); timed last, as it changes them
@@ -294,15 +366,8 @@ def main():
                          (cfg.num_idx_heads, 64))]
     pl = msa.pools(wt["k_pool"], wt["v_pool"], wt["k_scale"], wt["v_scale"], wt["idx_k_pool"],
                    wt.get("idx_k_scale"))
-    for _ in range(args.warmup):
-        msa.msa_insert_kv(p, pl, wt["block_table"], wt["ctx_lens"], *new)
-    torch.cuda.synchronize()
-    start.record()
-    for _ in range(args.steps):
-        msa.msa_insert_kv(p, pl, wt["block_table"], wt["ctx_lens"], *new)
-    end.record()
-    torch.cuda.synchronize()
-    insert_us = start.elapsed_time(end) / args.steps * 1e3
+    insert_us = time_loop(lambda: msa.msa_insert_kv(p, pl, wt["block_table"], wt["ctx_lens"],
+                                                    *new), args.steps, args.warmup)
 
     rec = {
         "metric": METRIC,
@@ -318,11 +383,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": f"{cfg.name}: batch {cfg.batch}, decode_query_len {cfg.query_len}, "
-                        f"context U[{cfg.ctx_lo}, {cfg.ctx_hi}], heads q/kv/idx "
-                        f"{cfg.num_q_heads}/{cfg.num_kv_heads}/{cfg.num_idx_heads}, "
-                        f"KV {cfg.kv_dtype}, index keys {cfg.idx_dtype}, top-{cfg.topk} "
-                        f"blocks of 128 with the local block",
+            "workload": describe_workload(cfg),
             "batch": cfg.batch,
             "decode_query_len": cfg.query_len,
             "mean_context": sum(w.ctx_lens) / cfg.batch,
@@ -331,6 +392,8 @@ def main():
             "frac_of_peak_end_to_end": ab["total"] / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
             "kernels": dispatch,
             "step_us_after_cache_flush": cold_us,
+            "frac_of_peak_end_to_end_after_cache_flush":
+                ab["total"] / (cold_us["p50"] * 1e-6) / 1e9 / PEAK_HBM_GBS,
             "insert": {
                 "us": insert_us,
                 "rows": R,
@@ -354,8 +417,33 @@ def main():
             "traffic": measured_traffic(cfg.name),
         },
     }
+    cpu = None
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_requests)
+        cpu = cpu_baseline(w, args.cpu_requests)
+        cpu["cpu"] = cpu_model()
+        cpu["host_cpus"] = os.cpu_count()
+    del tw, w, wt, p, t, o_out, ws, pt, new, pl
+    torch.cuda.empty_cache()
+
+    # the other configurations: their own step records (not the headline)
+    if not args.no_other_workloads:
+        others = {}
+        for name in CONFIG_ORDER + EXTRA_CONFIGS:
+            if name == cfg.name:
+                continue
+            others[name] = workload_record(CONFIGS[name], min(args.steps, 20), args.warmup,
+                                           min(args.steps, 10))
+            # single-core oracle baselines of the two smallest configurations
+            if cpu is not None and name in ("tiny_4k", "tp8_rank_32k"):
+                from synth import make_workload
+                wsmall = make_workload(CONFIGS[name], "cuda")
+                cpu.setdefault("single_core", {})[name] = cpu_baseline(
+                    wsmall, 1 if name == "tiny_4k" else 8, threads=1)
+                del wsmall
+                torch.cuda.empty_cache()
+        rec["other_workloads"] = others
+    if cpu is not None:
+        rec["cpu_baseline"] = cpu
     print(json.dumps(rec), flush=True)
 
 

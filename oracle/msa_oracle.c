@@ -496,3 +496,13 @@ int msa_oracle_num_threads(void) {
   return 1;
 #endif
 }
+
+/* Sets the number of worker threads of the parallel loops above (the
+ * benchmark's single-core baseline uses 1); n < 1 leaves it unchanged. */
+void msa_oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}

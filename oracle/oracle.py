@@ -103,6 +103,8 @@ def lib():
         L.msa_oracle_attention.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                            ctypes.c_int32, vp]
         L.msa_oracle_num_threads.restype = ctypes.c_int
+        L.msa_oracle_set_num_threads.argtypes = [ctypes.c_int]
+        L.msa_oracle_set_num_threads.restype = None
         L.msa_oracle_f32_to_e4m3.restype = ctypes.c_uint8
         L.msa_oracle_f32_to_e4m3.argtypes = [ctypes.c_float]
         L.msa_oracle_f32_to_e2m1.restype = ctypes.c_uint8
@@ -258,3 +260,8 @@ def insert(prob, k_new, v_new, idx_new, block_table, ctx_lens, pools):
 
 def num_threads() -> int:
     return int(lib().msa_oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Worker threads of the oracle's parallel loops (1: a single core)."""
+    lib().msa_oracle_set_num_threads(int(n))
