@@ -373,6 +373,34 @@ __device__ __forceinline__ void select_request(int b, const float* __restrict__ 
     }
     __syncthreads();
 
+    // 8 waves (one row): every wave ranks 16 of the (up to kCap) entries by
+    // counting, each lane against a quarter of the entries, instead of one
+    // wave ranking them all (the entries are the survivors, or on the list
+    // path the waves' picks, zeros ranking below every key).
+    if constexpr (NW == 8) {
+      if (work) {
+        const int me = list_path ? parts * K1 : m;
+        const uint64_t* sv_ = sh.survivors[slot];
+        const int i = 16 * wave + (lane & 15);
+        const int quarter = lane >> 4;
+        const uint64_t e = i < me ? sv_[i] : 0;
+        int cnt = 0;
+        // 8 independent reads per step (kCap = 128 entries: at most 4 steps)
+        for (int j0 = quarter; j0 < me; j0 += 32) {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const int j = j0 + 4 * q;
+            const uint64_t x = sv_[min(j, kCap - 1)];
+            cnt += (j < me && x > e) ? 1 : 0;
+          }
+        }
+        cnt += __shfl_xor(cnt, 16);
+        cnt += __shfl_xor(cnt, 32);
+        if (quarter == 0 && i < me && e != 0 && cnt < K1) row_sel[slot][cnt] = key_id(e);
+      }
+      __syncthreads();
+    }
+
     if (active && part == 0) {
       int n = 0;
       if (take_all) {
@@ -383,11 +411,12 @@ __device__ __forceinline__ void select_request(int b, const float* __restrict__ 
         n = 1;
       } else {
         // the K1 best keys go to row_sel[wave][rank] (keys are unique, so
-        // ranks 0 .. K1 - 1 each have exactly one owner)
-        if (!list_path || NW == 8) {
-          // rank by counting among the survivors, or (8 waves, list path)
-          // among the waves' picks, which may hold zeros
-          const int me = list_path ? parts * K1 : m;
+        // ranks 0 .. K1 - 1 each have exactly one owner); with 8 waves that
+        // happened above
+        if (NW == 8) {
+        } else if (!list_path) {
+          // rank by counting among the survivors
+          const int me = m;
           uint64_t* sv_ = sh.survivors[slot];
           const uint64_t e0 = lane < me ? sv_[lane] : 0;
           const uint64_t e1 = lane + kWave < me ? sv_[lane + kWave] : 0;
@@ -406,9 +435,8 @@ __device__ __forceinline__ void select_request(int b, const float* __restrict__ 
               r1 += x > e1 ? 1 : 0;
             }
           }
-          if (lane < me && (NW == 4 || e0 != 0) && r0 < K1) row_sel[wave][r0] = key_id(e0);
-          if (lane + kWave < me && (NW == 4 || e1 != 0) && r1 < K1)
-            row_sel[wave][r1] = key_id(e1);
+          if (lane < me && r0 < K1) row_sel[wave][r0] = key_id(e0);
+          if (lane + kWave < me && r1 < K1) row_sel[wave][r1] = key_id(e1);
         } else {
           // merge-rank of the waves' picks: each wave's list is sorted best
           // first (zeros last) and keys are unique, so a pick's rank is its
@@ -430,7 +458,8 @@ __device__ __forceinline__ void select_request(int b, const float* __restrict__ 
           }
           if (lane < mf && rank < K1 && mine != 0) row_sel[wave][rank] = key_id(mine);
         }
-        // order the K1 winners by id: lane k places the k-th ranked one
+        // order the K1 winners by id: lane k places the k-th ranked one,
+        // its position counted from the other winners' ids in registers
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -438,7 +467,7 @@ __device__ __forceinline__ void select_request(int b, const float* __restrict__ 
         int posn = 0;
 #pragma unroll
         for (int e = 0; e < kList; ++e) {
-          const int o = e < K1 ? row_sel[wave][e] : INT32_MAX;
+          const int o = __builtin_amdgcn_readlane(id, e);
           posn += o < id ? 1 : 0;
         }
         __builtin_amdgcn_wave_barrier();
