@@ -69,3 +69,48 @@ def test_noalloc_without_exported_tables_and_repeats():
         msa.msa_decode_noalloc(p, t, None, None, out)
         torch.cuda.synchronize()
         assert torch.equal(out, want["out"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(batch=3, query_len=1, ctx_lo=1500, ctx_hi=9000, seed=46),
+    dict(batch=2, query_len=4, ctx_lo=3000, ctx_hi=20000, kv_dtype="fp8", idx_dtype="fp8",
+         seed=47),
+], ids=["bf16_T1_split", "fp8_T4"])
+def test_noalloc_captured_into_a_graph(kw):
+    """The case it exists for: captured once into a HIP graph (no allocation
+    inside the capture), replayed with the queries changed in place, each
+    replay equal bit for bit to msa_decode on a caller workspace."""
+    cfg = small_config(**kw)
+    w = make_workload(cfg, DEV)
+    t = w.tensors
+    p = problem_for(w)
+    tt = tensors_for(w)
+    R = cfg.rows
+    sel = torch.empty((R, cfg.topk), dtype=torch.int32, device=DEV)
+    pt = torch.empty((R, cfg.topk * 8), dtype=torch.int32, device=DEV)
+    out = torch.empty((R, cfg.num_q_heads, 128), dtype=torch.float32, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        msa.msa_decode_noalloc(p, tt, sel, pt, out)  # first call on the device: set-up
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        msa.msa_decode_noalloc(p, tt, sel, pt, out)
+    q0 = t["q"].clone()
+    iq0 = t["idx_q"].clone()
+    for step in range(3):
+        if step:
+            t["q"].copy_(q0.roll(step, dims=1))
+            t["idx_q"].copy_(iq0 * (step + 1))
+        out.fill_(float("nan"))
+        sel.fill_(-7)
+        pt.fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        want = run_fused(w)
+        assert torch.equal(sel, want["selected"]), step
+        assert torch.equal(pt, want["page_table"]), step
+        assert torch.equal(out, want["out"]), step
