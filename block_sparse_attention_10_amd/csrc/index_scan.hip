@@ -229,7 +229,7 @@ __device__ __forceinline__ float row16_max(float v) {
 // 16 lanes of a DPP row gives the block score.  Products of bf16 values are
 // exact in fp32 and the synthetic sums stay below 2^24, so the scores equal
 // the VALU path's bit for bit.
-template <int KIND>
+template <int KIND, bool ONE_HEAD>
 __device__ __forceinline__ void scan_block_mfma(const uint16_t* __restrict__ idx_q,
                                                 const uint8_t* __restrict__ idx_k,
                                                 int phys_block, float* __restrict__ scores,
@@ -242,13 +242,13 @@ __device__ __forceinline__ void scan_block_mfma(const uint16_t* __restrict__ idx
   const size_t head_bytes = (size_t)kBlock * TB;
   const uint8_t* kblk = idx_k + (size_t)phys_block * Hidx * head_bytes;
   const u32x4 zero = {0u, 0u, 0u, 0u};
+  float* srow = scores + (size_t)b * T * MAXB + c;
+  const int tok0 = c * kBlock + n;
 
-  f32x4 acc[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int h = 0; h < Hidx; ++h) {
+  // one head's key loads (tile i: token 16 i + n, this lane's dims) and
+  // query operands (row n of the request, zeros past T)
+  auto load_keys = [&](u32x4 (&kv)[8][NL], int h) {
     const uint8_t* kh = kblk + (size_t)h * head_bytes;
-    u32x4 kv[8][NL];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const uint8_t* kt = kh + (size_t)(16 * i + n) * TB;
@@ -259,8 +259,10 @@ __device__ __forceinline__ void scan_block_mfma(const uint16_t* __restrict__ idx
         kv[i][0] = ldg128_stream(kt + 16 * g);
       }
     }
-    // row n of the request (zeros past T), the dims of this lane's k-group
-    u32x4 qa[2] = {zero, zero};
+  };
+  auto load_query = [&](u32x4 (&qa)[2], int h) {
+    qa[0] = zero;
+    qa[1] = zero;
     if (n < T) {
       const uint16_t* qp = idx_q + ((size_t)(b * T + n) * Hidx + h) * kIdxDim;
       if constexpr (KIND == kBf16) {
@@ -271,49 +273,81 @@ __device__ __forceinline__ void scan_block_mfma(const uint16_t* __restrict__ idx
         qa[1] = ldg128(qp + 16 * g + 8);
       }
     }
+  };
+  // tile i of one head added to `a`
+  auto tile = [&](f32x4 a, const u32x4 (&kv)[8][NL], const u32x4 (&qa)[2], int i) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        u32x4 kb;
-        if constexpr (KIND == kBf16) {
-          kb = kv[i][st];
-        } else {
-          const uint32_t lo = st ? kv[i][0].z : kv[i][0].x;
-          const uint32_t hi = st ? kv[i][0].w : kv[i][0].y;
-          kb.x = e4m3x2_to_bf16x2<false>(lo);
-          kb.y = e4m3x2_to_bf16x2<true>(lo);
-          kb.z = e4m3x2_to_bf16x2<false>(hi);
-          kb.w = e4m3x2_to_bf16x2<true>(hi);
-        }
-        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[st]),
-                                                         __builtin_bit_cast(bf16x8, kb), acc[i],
-                                                         0, 0, 0);
+    for (int st = 0; st < 2; ++st) {
+      u32x4 kb;
+      if constexpr (KIND == kBf16) {
+        kb = kv[i][st];
+      } else {
+        const uint32_t lo = st ? kv[i][0].z : kv[i][0].x;
+        const uint32_t hi = st ? kv[i][0].w : kv[i][0].y;
+        kb.x = e4m3x2_to_bf16x2<false>(lo);
+        kb.y = e4m3x2_to_bf16x2<true>(lo);
+        kb.z = e4m3x2_to_bf16x2<false>(hi);
+        kb.w = e4m3x2_to_bf16x2<true>(hi);
       }
+      a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[st]),
+                                                  __builtin_bit_cast(bf16x8, kb), a, 0, 0, 0);
     }
-  }
+    return a;
+  };
+  // rows 4 g + j: the max over this lane's causal tokens, then over the 16
+  // lanes of the DPP row
+  float best[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  auto fold = [&](const f32x4& a, int i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (tok0 + 16 * i <= L - T + 4 * g + j) best[j] = fmaxf(best[j], a[j]);
+  };
 
-  // rows 4 g + j: max over this lane's causal tokens 16 i + n, then over the
-  // 16 lanes of the DPP row
-  float* srow = scores + (size_t)b * T * MAXB + c;
-  const int tok0 = c * kBlock + n;
+  if constexpr (ONE_HEAD) {
+    // one index head: each tile is final as soon as it is computed, so only
+    // one accumulator is live (fewer registers, more waves in flight)
+    u32x4 kv[8][NL], qa[2];
+    load_keys(kv, 0);
+    load_query(qa, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) fold(tile(f32x4{0.f, 0.f, 0.f, 0.f}, kv, qa, i), i);
+  } else {
+    // the head sum comes before the max: all 8 tiles stay live over heads
+    f32x4 acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int h = 0; h < Hidx; ++h) {
+      u32x4 kv[8][NL], qa[2];
+      load_keys(kv, h);
+      load_query(qa, h);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = tile(acc[i], kv, qa, i);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) fold(acc[i], i);
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int row = 4 * g + j;
-    const int pos = L - T + row;
-    float best = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (tok0 + 16 * i <= pos) best = fmaxf(best, acc[i][j]);
-    best = row16_max(best);
-    if (n == 0 && row < T) srow[(size_t)row * MAXB] = best;
+    const float m = row16_max(best[j]);
+    if (n == 0 && 4 * g + j < T) srow[(size_t)(4 * g + j) * MAXB] = m;
   }
 }
 
 // msa_index_score: one wave per (request, logical block); blocks past the
-// context score -inf for every row.  TR 0: the matrix-core path.
+// context score -inf for every row.  TR 0: the matrix-core path; TR -1:
+// the matrix-core path for one index head.
+//
+// The single-row 4-bit scan holds only 4.5 KB per wave in flight (one
+// head's codes and scales), so it needs many waves: built for 6 waves per
+// SIMD (at most 80 registers; 76 used, no spills) it scanned the 128K layer
+// with 4-bit keys in 88.6 us against 93.3 us at the 112 registers the
+// compiler picks on its own (4 waves per SIMD); 5 waves per SIMD took 95.8
+// and 7 spill.
+constexpr int kFp4SingleRowWavesPerSimd = 6;
+
 template <int KIND, int TR>
-__global__ __launch_bounds__(256) void index_scan_kernel(
+__global__ __launch_bounds__(256, KIND == kFp4 && TR == 1 ? kFp4SingleRowWavesPerSimd : 1)
+void index_scan_kernel(
     const uint16_t* __restrict__ idx_q, const uint8_t* __restrict__ idx_k,
     const uint8_t* __restrict__ idx_ks, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ ctx_lens, float* __restrict__ scores, int B, int T, int Hidx,
@@ -335,7 +369,9 @@ __global__ __launch_bounds__(256) void index_scan_kernel(
     return;
   }
   if constexpr (TR == 0)
-    scan_block_mfma<KIND>(idx_q, idx_k, phys, scores, b, c, L, T, Hidx, MAXB, lane);
+    scan_block_mfma<KIND, false>(idx_q, idx_k, phys, scores, b, c, L, T, Hidx, MAXB, lane);
+  else if constexpr (TR < 0)
+    scan_block_mfma<KIND, true>(idx_q, idx_k, phys, scores, b, c, L, T, Hidx, MAXB, lane);
   else
     scan_block<KIND, TR>(idx_q, idx_k, idx_ks, phys, scores, b, c, L, T, Hidx, MAXB, lane);
 }
@@ -376,11 +412,14 @@ hipError_t launch_kind(const Dims& d, const void* idx_q, const void* idx_k, cons
   const auto* ks = static_cast<const uint8_t*>(idx_ks);
   const bool mfma = (KIND == kBf16 && d.T >= kMfmaMinRowsBf16) ||
                     (KIND == kFp8 && d.T >= kMfmaMinRowsFp8);
-  const int tr = mfma ? 0 : (d.T == 1 ? 1 : (d.T == 2 ? 2 : 4));
+  const int tr = mfma ? (d.Hidx == 1 ? -1 : 0) : (d.T == 1 ? 1 : (d.T == 2 ? 2 : 4));
   const size_t lds = mfma ? 0 : scan_lds_bytes(KIND, grid.x);
   if constexpr (KIND != kFp4) {
     if (tr == 0)
       hipLaunchKernelGGL((index_scan_kernel<KIND, 0>), grid, block, lds, s, q, k, ks, bt, cl,
+                         scores, d.B, d.T, d.Hidx, d.MAXB, d.NB - 1);
+    else if (tr == -1)
+      hipLaunchKernelGGL((index_scan_kernel<KIND, -1>), grid, block, lds, s, q, k, ks, bt, cl,
                          scores, d.B, d.T, d.Hidx, d.MAXB, d.NB - 1);
   }
   if (tr == 1)
@@ -395,7 +434,7 @@ hipError_t launch_kind(const Dims& d, const void* idx_q, const void* idx_k, cons
   static const char* names[3] = {"bf16", "fp8", "nvfp4"};
   if (note)
     *note += std::string("index_scan<") + names[KIND] +
-             (tr == 0 ? std::string(",mfma") : ",rows" + std::to_string(tr)) +
+             (tr <= 0 ? std::string(tr ? ",mfma1" : ",mfma") : ",rows" + std::to_string(tr)) +
              ">[grid=" + std::to_string(grid.x) + "x256,lds=" + std::to_string(lds) + "]";
   return hipGetLastError();
 }
