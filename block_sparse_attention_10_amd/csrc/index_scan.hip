@@ -173,7 +173,7 @@ __device__ __forceinline__ void scan_block(const uint16_t* __restrict__ idx_q,
       for (int i = 0; i < NLD; ++i) part[t][i] = 0.f;
 
     // (keeping the next head's loads in flight was measured no faster for
-    // 4-bit keys: it costs occupancy that 16 waves per CU already cover)
+    // 4-bit keys: it costs the occupancy that the 4-bit scan relies on)
     for (int h = 0; h < Hidx; ++h) {
       Head hd;
       load_head(hd, h, t0);
