@@ -834,9 +834,23 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 1 : 2) void union_attn_kernel(
       for (int jp = 0; jp < 2; ++jp) stage_v<KV>(ch[jp], stage + 16 * jp * kVRow, lane);
     }
 
+    // logit scale per key: the softmax scale (log2 domain) times the fp8
+    // K scale, shared by the tiles
+    float ks[2][4];
+#pragma unroll
+    for (int jp = 0; jp < 2; ++jp)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ks[jp][i] = scale_log2;
+        if constexpr (KV == 1) ks[jp][i] = scale_log2 * ch[jp].kscale[i];
+      }
+    // a skipped tile keeps zero P, so its P V products below add nothing
     bf16x8 phi[NT], plo[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
+      const u32x4 z4 = {0u, 0u, 0u, 0u};
+      phi[j] = __builtin_bit_cast(bf16x8, z4);
+      plo[j] = phi[j];
       if (!(bits & tmask[j])) continue;
       // S^T = K Q^T for the two pages, this tile's columns
       f32x4 sacc[2];
@@ -859,24 +873,27 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 1 : 2) void union_attn_kernel(
       for (int jp = 0; jp < 2; ++jp)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float v = sacc[jp][i] * scale_log2;
-          if constexpr (KV == 1) v *= ch[jp].kscale[i];
+          float v = sacc[jp][i] * ks[jp][i];
           const int tok = 16 * (pg0 + jp) + 4 * g4 + i;
           v = tok < lim ? v : neg_inf();
           z[4 * jp + i] = v;
           mc = fmaxf(mc, v);
         }
       mc = fmaxf(mc, __shfl_xor(mc, 16));
-      mc = fmaxf(mc, __shfl_xor(mc, 32));
+    mc = fmaxf(mc, __shfl_xor(mc, 32));
       const float mn = fmaxf(m[j], mc);
-      const float alpha = mn == m[j] ? 1.f : __builtin_amdgcn_exp2f(m[j] - mn);
+      // exponents relative to a finite maximum: masked logits (-inf) give
+      // exactly 0, an unchanged maximum gives alpha = 1, and a column with
+      // nothing unmasked yet keeps zero sums
+      const float mref = mn == neg_inf() ? 0.f : mn;
+      const float alpha = __builtin_amdgcn_exp2f(m[j] - mref);
       m[j] = mn;
       // P as bf16 hi + lo (two values per conversion), V scales folded in
       float psum = 0.f;
       float pv[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float pe = z[e] == neg_inf() ? 0.f : __builtin_amdgcn_exp2f(z[e] - mn);
+        const float pe = __builtin_amdgcn_exp2f(z[e] - mref);
         psum += pe;
         pv[e] = pe;
         if constexpr (KV == 1) pv[e] *= ch[e >> 2].vscale[e & 3];
@@ -928,7 +945,6 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 1 : 2) void union_attn_kernel(
       }
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
-        if (!(bits & tmask[j])) continue;
         oacc[j][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, phi[j], oacc[j][s], 0, 0, 0);
         oacc[j][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, plo[j], oacc[j][s], 0, 0, 0);
       }
