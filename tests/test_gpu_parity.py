@@ -69,6 +69,37 @@ SMALL = [
 ]
 
 
+# Every scan path (index_scan.hip: VALU passes of 1 / 2 / 4 rows, the matrix-core
+# scan for one index head and for several), with the dispatch that must run.
+SCAN_PATHS = [
+    ("bf16", 1, 2, "rows1"), ("bf16", 2, 2, "rows2"), ("bf16", 4, 1, "rows4"),
+    ("bf16", 5, 1, "mfma1"), ("bf16", 6, 3, "mfma"),
+    ("fp8", 1, 3, "rows1"), ("fp8", 2, 1, "mfma1"), ("fp8", 3, 2, "mfma"),
+    ("nvfp4", 1, 4, "rows1"), ("nvfp4", 3, 2, "rows4"),
+]
+
+
+@pytest.mark.parametrize("idx_dtype,T,hidx,path", SCAN_PATHS,
+                         ids=[f"{d}-T{t}-H{h}" for d, t, h, _ in SCAN_PATHS])
+def test_index_scan_paths(idx_dtype, T, hidx, path):
+    cfg = small_config(batch=3, query_len=T, ctx_lo=100, ctx_hi=7000, idx_dtype=idx_dtype,
+                       num_idx_heads=hidx, seed=60 + T + 7 * hidx)
+    _say(f"scan path {idx_dtype} T={T} Hidx={hidx} (expect {path})")
+    w = make_workload(cfg, DEV)
+    p = problem_for(w)
+    scores = torch.full((cfg.rows, cfg.max_blocks), 7.0, dtype=torch.float32, device=DEV)
+    msa.msa_index_score(p, tensors_for(w), scores)
+    torch.cuda.synchronize()
+    assert f"index_scan<{idx_dtype},{path}>" in msa.msa_last_dispatch()
+    rows = list(range(cfg.rows))
+    ref = oracle_rows(w, rows)
+    got = scores.cpu().numpy()
+    for r in rows:
+        nb = ref[r]["scores"].shape[0]
+        assert np.array_equal(got[r][:nb].astype(np.float64), ref[r]["scores"]), f"row {r}"
+        assert np.all(np.isneginf(got[r][nb:])), f"tail of row {r}"
+
+
 @pytest.mark.parametrize("kw", SMALL, ids=[str(i) for i in range(len(SMALL))])
 def test_small_shapes_stagewise_and_fused(kw):
     cfg = small_config(**kw)
