@@ -178,8 +178,9 @@ int decode_with_workspace(const Dims& d, const msa_tensors* t, int32_t* selected
                                         t->block_table, t->ctx_lens, scores, s, &note))))
     return e;
   note += " ";
-  // Single-row requests select inside the attention launch (one launch
-  // fewer on the dependent chain); the rest select in a launch of their own.
+  // Single-row requests, and multi-row requests that walk their union,
+  // select inside the attention launch (one launch fewer on the dependent
+  // chain); the rest select in a launch of their own.
   const bool fuse = fused_select_eligible(d);
   const SelectArgs fused{scores, t->block_table, selected, nullptr, page_table};
   if (!fuse) {

@@ -37,10 +37,11 @@
 //  * fp8 K/V: e4m3 -> bf16 is exact; the per-token K scale multiplies the
 //    logit, the V scale multiplies P.  4-bit K/V: e2m1 x e4m3 -> bf16 is
 //    exact (at most 6 significant bits) and happens in registers.
-//  * Inside msa_decode, single-row requests select in this launch: every
-//    workgroup of a row runs the selection (select_device.h) on the row's
-//    block scores first and keeps the page ids in LDS, which saves the
-//    selection launch on the dependent chain.
+//  * Inside msa_decode, single-row requests and multi-row requests that
+//    walk their union select in this launch: every workgroup of a row (of a
+//    request) runs the selection (select_device.h) on the block scores first
+//    and keeps the page ids in LDS, which saves the selection launch on the
+//    dependent chain.
 //  * Split partials (m, l, unnormalised O) combine inside the workgroup in
 //    LDS; when a row is split over several workgroups a small merge kernel
 //    applies the log-sum-exp rule.  (Merging in the last workgroup to finish
@@ -687,15 +688,17 @@ constexpr int kDmaPerChunk = 9;  // direct-to-LDS loads per prefetched fp8 chunk
 
 // Every wave computes all NT tiles of each of its chunks, so each union
 // block is loaded once per request.  fp8 (D > 0): each wave keeps up to D
-// chunks in flight in a ring of LDS slots.
-template <int KV, int W, int NT, int D>
+// chunks in flight in a ring of LDS slots.  SEL: the workgroup first
+// selects the request's rows itself (its first four waves, from the block
+// scores; page ids into LDS) instead of reading a page table.
+template <int KV, int W, int NT, int D, bool SEL>
 __global__ __launch_bounds__(64 * W, W == 4 ? 1 : 2) void union_attn_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ k_pool,
     const uint8_t* __restrict__ v_pool, const void* __restrict__ k_scale,
     const void* __restrict__ v_scale, const int32_t* __restrict__ page_table,
     const int32_t* __restrict__ ctx_lens, float* __restrict__ part_o,
     float* __restrict__ part_ml, float* __restrict__ out, int B, int T, int Hq, int Hkv, int PT,
-    int S, int max_block, float scale_log2) {
+    int S, int max_block, float scale_log2, SelectArgs sa, int MAXB) {
   constexpr bool kPrefetch = D > 0;
   static_assert(!kPrefetch || KV == 1, "prefetch ring for fp8 chunks");
   static_assert(D <= 3, "vmcnt waits below cover up to 3 chunks in flight");
@@ -746,8 +749,23 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 1 : 2) void union_attn_kernel(
       if (r * G < 16 * j + 16 && (r + 1) * G > 16 * j) tmask[j] |= 1 << r;
   }
 
-  int u_phys, u_bits;
-  const int nU = union_of_rows(page_table, b, T, PT, lane, u_phys, u_bits);
+  int u_phys, u_bits, nU;
+  if constexpr (SEL) {
+    // every (KV head, split) workgroup of the request selects (T <= 4 rows,
+    // one wave each); the (0, 0) one exports.  The selection's LDS and the
+    // rows' page ids sit in the staging area, free until the chunk loop.
+    static_assert(W >= 4, "four selecting waves");
+    auto* ssh = reinterpret_cast<SelectLds<4>*>(smem);
+    int32_t* prow = reinterpret_cast<int32_t*>(smem + ((sizeof(SelectLds<4>) + 15) & ~15));
+    const bool exporter = g == 0 && split == 0;
+    select_request<4, W>(b, sa.scores, ctx_lens, sa.block_table,
+                         exporter ? sa.selected : nullptr, exporter ? sa.n_selected : nullptr,
+                         exporter ? sa.page_table : nullptr, T, MAXB, PT / 8, *ssh, prow);
+    nU = union_of_rows(prow, 0, T, PT, lane, u_phys, u_bits);
+    __syncthreads();  // the page ids are read: the staging area is free
+  } else {
+    nU = union_of_rows(page_table, b, T, PT, lane, u_phys, u_bits);
+  }
   const int nchunks = 4 * nU;
 
   float m[NT], lsum[NT];
@@ -1077,19 +1095,19 @@ long attention_workgroups(const Dims& d, const SplitPlan& sp) {
 constexpr int kUnionWavesFp8 = 8;
 constexpr int kUnionDepthFp8 = 1;
 
-template <int KV, int NT>
+template <int KV, int NT, bool SEL>
 hipError_t launch_union(const Dims& d, const SplitPlan& sp, const void* q, const void* k_pool,
                         const void* v_pool, const void* k_scale, const void* v_scale,
                         const int32_t* page_table, const int32_t* ctx_lens, float* part_o,
-                        float* part_ml, float* out, hipStream_t s) {
+                        float* part_ml, float* out, const SelectArgs& sa, hipStream_t s) {
   constexpr int W = KV == 1 ? kUnionWavesFp8 : 8;
   constexpr int D = KV == 1 ? kUnionDepthFp8 : 0;
-  hipLaunchKernelGGL((union_attn_kernel<KV, W, NT, D>),
+  hipLaunchKernelGGL((union_attn_kernel<KV, W, NT, D, SEL>),
                      dim3((unsigned)attention_workgroups(d, sp)), dim3(64 * W), 0, s,
                      static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(k_pool),
                      static_cast<const uint8_t*>(v_pool), k_scale, v_scale, page_table,
                      ctx_lens, part_o, part_ml, out, d.B, d.T, d.Hq, d.Hkv, d.PT(), sp.splits,
-                     d.NB - 1, d.scale_log2);
+                     d.NB - 1, d.scale_log2, sa, d.MAXB);
   return hipGetLastError();
 }
 
@@ -1113,11 +1131,19 @@ hipError_t launch_kv(const Dims& d, const SplitPlan& sp, const void* q, const vo
                      const int32_t* page_table, const int32_t* ctx_lens, float* part_o,
                      float* part_ml, float* out, const SelectArgs* sel, hipStream_t s) {
   if (sp.rows_union) {
+    const SelectArgs none{};
+    if (sel) {
+      if (sp.tiles == 1)
+        return launch_union<KV, 1, true>(d, sp, q, k_pool, v_pool, k_scale, v_scale, nullptr,
+                                         ctx_lens, part_o, part_ml, out, *sel, s);
+      return launch_union<KV, 2, true>(d, sp, q, k_pool, v_pool, k_scale, v_scale, nullptr,
+                                       ctx_lens, part_o, part_ml, out, *sel, s);
+    }
     if (sp.tiles == 1)
-      return launch_union<KV, 1>(d, sp, q, k_pool, v_pool, k_scale, v_scale, page_table,
-                                 ctx_lens, part_o, part_ml, out, s);
-    return launch_union<KV, 2>(d, sp, q, k_pool, v_pool, k_scale, v_scale, page_table,
-                               ctx_lens, part_o, part_ml, out, s);
+      return launch_union<KV, 1, false>(d, sp, q, k_pool, v_pool, k_scale, v_scale, page_table,
+                                        ctx_lens, part_o, part_ml, out, none, s);
+    return launch_union<KV, 2, false>(d, sp, q, k_pool, v_pool, k_scale, v_scale, page_table,
+                                      ctx_lens, part_o, part_ml, out, none, s);
   }
   if (sel)
     return launch_kvw<KV, 8, true>(d, sp, q, k_pool, v_pool, k_scale, v_scale, nullptr,
@@ -1170,7 +1196,8 @@ SplitPlan plan_splits(const Dims& d) {
 constexpr int kFusedSelectMaxBlocks = 16384;
 
 bool fused_select_eligible(const Dims& d) {
-  return d.T == 1 && d.MAXB <= kFusedSelectMaxBlocks && plan_splits(d).waves == 8;
+  if (d.MAXB > kFusedSelectMaxBlocks) return false;
+  return union_eligible(d) || (d.T == 1 && plan_splits(d).waves == 8);
 }
 
 hipError_t launch_sparse_attention(const Dims& d, const void* q, const void* k_pool,

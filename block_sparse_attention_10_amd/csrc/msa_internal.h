@@ -53,9 +53,10 @@ hipError_t launch_page_table(const Dims& d, const int32_t* selected, const int32
                              int32_t* page_table, hipStream_t s, std::string* note);
 
 // Inputs of the selection an attention workgroup runs itself when the
-// selection is fused into the attention launch (single-row requests).  The
-// (KV head 0, split 0) workgroup of each row exports its selection and page
-// ids to selected / n_selected / page_table when those are not null.
+// selection is fused into the attention launch (single-row requests, and
+// multi-row requests that walk their union).  The (KV head 0, split 0)
+// workgroup of each row (request) exports its selection and page ids to
+// selected / n_selected / page_table when those are not null.
 struct SelectArgs {
   const float* scores;
   const int32_t* block_table;

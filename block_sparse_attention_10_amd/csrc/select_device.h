@@ -192,10 +192,11 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
 }
 
 // Selection (and, when page_table is given, the page table) for every row of
-// request b.  Called by all threads of an NW-wave workgroup (NW = 8 only for
-// single-row requests); contains workgroup barriers.  page_row (LDS, single-
-// row requests): the row's page ids are also left there, visible to the
-// whole workgroup on return.
+// request b.  Called by all threads of an NW-wave workgroup, of which the
+// first NWS select (NWS = 8 only for single-row requests; the other waves
+// only take part in the barriers); contains workgroup barriers.  page_row
+// (LDS, T x topk x 8 ids): the rows' page ids are also left there, visible
+// to the whole workgroup on return.
 //
 // Per row: every lane takes the best key among its candidates; each wave
 // finds the K1-th best of its lane maxima (K1 = topk - 1) by counting.  That key has
@@ -206,19 +207,21 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
 // the best keys) take the list path instead: per-lane sorted lists of the
 // K1 best keys, K1 wave-max pops per wave, and a merge-rank of the waves'
 // picks.
-template <int NW>
+template <int NWS, int NW = NWS>
 __device__ __forceinline__ void select_request(int b, const float* __restrict__ scores,
                                             const int32_t* __restrict__ ctx_lens,
                                             const int32_t* __restrict__ block_table,
                                             int32_t* __restrict__ selected,
                                             int32_t* __restrict__ n_selected,
                                             int32_t* __restrict__ page_table, int T, int MAXB,
-                                            int topk, SelectLds<NW>& sh,
+                                            int topk, SelectLds<NWS>& sh,
                                             int32_t* page_row = nullptr) {
+  static_assert(NW >= NWS, "the selecting waves are the first NWS of the workgroup");
   const int lane = lane_id();
   const int wave = wave_id();
-  const int parts = NW == 8 ? 8 : (T >= 4 ? 1 : (T == 1 ? 4 : (T == 2 ? 2 : 1)));
-  const int rows_per_pass = NW / parts;
+  const bool member = NW == NWS || wave < NWS;  // wave-uniform
+  const int parts = NWS == 8 ? 8 : (T >= 4 ? 1 : (T == 1 ? 4 : (T == 2 ? 2 : 1)));
+  const int rows_per_pass = NWS / parts;
   const int K1 = topk - 1;
   const int stride = parts * kWave;
   const int part = wave % parts;
@@ -233,10 +236,13 @@ __device__ __forceinline__ void select_request(int b, const float* __restrict__ 
     // round trips overlap; the empty asm pins the loads ahead of the branches
     // that use them.
     float sv[kBatch];
-    {
+    if (member) {
       const float* srow = scores + (size_t)(b * T + min(t, T - 1)) * MAXB;
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) sv[u] = srow[min(cfirst + u * stride, MAXB - 1)];
+    } else {
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) sv[u] = 0.f;
     }
     int L = ctx_lens[b];
 #pragma unroll
@@ -245,7 +251,7 @@ __device__ __forceinline__ void select_request(int b, const float* __restrict__ 
     // a context longer than its table row cannot send the candidates (and
     // the table lookups of the page build) past the row
     L = min(L, MAXB * 128);
-    const bool active = t < T;
+    const bool active = member && t < T;
     const int r = b * T + t;
     const float* srow = scores + (size_t)r * MAXB;
     const int pos = L - T + t;
@@ -253,11 +259,11 @@ __device__ __forceinline__ void select_request(int b, const float* __restrict__ 
     const bool take_all = local + 1 <= topk;
     // uniform over the row's waves
     const bool work = active && !take_all && K1 > 0;
-    if (part == 0 && lane == 0) sh.count[slot] = 0;
+    if (member && part == 0 && lane == 0) sh.count[slot] = 0;
 
     // lane maxima; the orderable scores of the first two batches (one with
     // 8 waves, which keeps the registers below 256) stay in registers
-    constexpr bool kTwo = NW == 4;
+    constexpr bool kTwo = NWS == 4 && NW == 4;
     float sv2[kBatch];
     uint32_t ok0[kBatch], ok1[kBatch];
     const int c1 = cfirst + kBatch * stride;
@@ -286,12 +292,12 @@ __device__ __forceinline__ void select_request(int b, const float* __restrict__ 
       const uint64_t at = __ballot(lmax != 0 && above == K1 - 1);
       if (at) wbound = lane_key(lmax, __builtin_ctzll(at));
     }
-    if (lane == 0) sh.bound[wave] = wbound;
+    if (member && lane == 0) sh.bound[wave] = wbound;
     __syncthreads();
 
     // survivors: keys at or above the largest bound of the row's waves
     uint64_t bound = 0;
-    for (int q = 0; q < parts; ++q) {
+    for (int q = 0; q < parts && member; ++q) {
       const uint64_t x = sh.bound[slot * parts + q];
       bound = x > bound ? x : bound;
     }
@@ -343,7 +349,7 @@ __device__ __forceinline__ void select_request(int b, const float* __restrict__ 
       }
     }
     __syncthreads();
-    const int m = sh.count[slot];
+    const int m = member ? sh.count[slot] : 0;
     const bool list_path = work && m > kCap;  // uniform over the row's waves
 
     if (list_path) {
@@ -356,7 +362,7 @@ __device__ __forceinline__ void select_request(int b, const float* __restrict__ 
         insert_batch(list, sx, c0, stride, local);
       }
       // this wave's K1 best keys, best first; 0 once its lists run dry
-      uint64_t* picks = (NW == 8 ? sh.survivors[slot] : sh.finalists) + wave * K1;
+      uint64_t* picks = (NWS == 8 ? sh.survivors[slot] : sh.finalists) + wave * K1;
       for (int k = 0; k < K1; ++k) {
         const uint64_t best = wave_max_u64(list[0]);
         if (best == 0) {  // wave-uniform
@@ -377,7 +383,7 @@ __device__ __forceinline__ void select_request(int b, const float* __restrict__ 
     // counting, each lane against a quarter of the entries, instead of one
     // wave ranking them all (the entries are the survivors, or on the list
     // path the waves' picks, zeros ranking below every key).
-    if constexpr (NW == 8) {
+    if constexpr (NWS == 8) {
       if (work) {
         const int me = list_path ? parts * K1 : m;
         const uint64_t* sv_ = sh.survivors[slot];
@@ -413,7 +419,7 @@ __device__ __forceinline__ void select_request(int b, const float* __restrict__ 
         // the K1 best keys go to row_sel[wave][rank] (keys are unique, so
         // ranks 0 .. K1 - 1 each have exactly one owner); with 8 waves that
         // happened above
-        if (NW == 8) {
+        if (NWS == 8) {
         } else if (!list_path) {
           // rank by counting among the survivors
           const int me = m;
@@ -490,7 +496,7 @@ __device__ __forceinline__ void select_request(int b, const float* __restrict__ 
           int v = -1;
           if (k < n) v = block_table[(size_t)b * MAXB + row_sel[wave][k]] * 8 + (e & 7);
           if (page_table) page_table[(size_t)r * pt + e] = v;
-          if (page_row) page_row[e] = v;
+          if (page_row) page_row[(size_t)t * pt + e] = v;
         }
       }
     }

@@ -229,9 +229,11 @@ int msa_insert_kv(const msa_problem* p, const msa_pools* pools, const int32_t* b
 
 /* Steps 1-4 in one call: the index scan, the selection with the page table
  * built in the same launch, then the attention (and its merge launch when
- * rows are split).  For single-row requests (decode_query_len 1) with at
- * most 16384 blocks per row, every attention workgroup selects its own
- * row's blocks at its start instead, and the selection launch is skipped.
+ * rows are split).  For single-row requests (decode_query_len 1), and for
+ * requests of 2-4 rows whose rows' query heads per KV head number at most
+ * 32, with at most 16384 blocks per row, every attention workgroup selects
+ * its rows' blocks at its start instead, and the selection launch is
+ * skipped.
  * selected / page_table may be NULL; when given they receive the step 2 /
  * step 3 results.  Block scores, counts and any table not supplied live in
  * `workspace`. */
