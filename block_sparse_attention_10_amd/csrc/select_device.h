@@ -129,24 +129,6 @@ __device__ __forceinline__ void key_batch(uint32_t (&ok)[kBatch], const float (&
   }
 }
 
-// Counts (WRITE false) or stores at out[0 .. room) (WRITE true) the keys of
-// a batch that reach `bound`; returns how many reach it.
-template <bool WRITE>
-__device__ __forceinline__ int pass_keys(const uint32_t (&ok)[kBatch], int c0, int stride,
-                                         uint64_t bound, int nw, uint64_t* out, int room) {
-  int n = 0;
-#pragma unroll
-  for (int u = 0; u < kBatch; ++u) {
-    if (u >= nw) break;  // wave-uniform
-    const uint64_t x = key_of(ok[u], c0 + u * stride);
-    if (ok[u] != 0 && x >= bound) {
-      if (WRITE && n < room) out[n] = x;
-      ++n;
-    }
-  }
-  return n;
-}
-
 // Inserts a batch of candidates (ids c0, c0 + stride, ...; those >= local
 // are skipped) into the lane's descending list of kList keys.
 __device__ __forceinline__ void insert_batch(uint64_t (&list)[kList], const float (&sv)[kBatch],
@@ -183,12 +165,6 @@ __device__ __forceinline__ uint64_t lane_key(uint64_t v, int j) {
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), j);
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, j);
   return ((uint64_t)hi << 32) | lo;
-}
-
-// Number of set bits of `m` in lanes below this one.
-__device__ __forceinline__ int lanes_below(uint64_t m) {
-  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                        __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
 // Selection (and, when page_table is given, the page table) for every row of
@@ -302,8 +278,22 @@ __device__ __forceinline__ void select_request(int b, const float* __restrict__ 
       bound = x > bound ? x : bound;
     }
     if (work) {
-      int mine = pass_keys<false>(ok0, cfirst, stride, bound, nw0, nullptr, 0);
-      if (kTwo) mine += pass_keys<false>(ok1, c1, stride, bound, nw1, nullptr, 0);
+      // every key at or above the bound takes the next survivor slot by an
+      // LDS atomic (the ranking below depends only on the keys, not on
+      // their order)
+      auto append = [&](const uint32_t (&ok)[kBatch], int c0, int nw) {
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          if (u >= nw) break;  // wave-uniform
+          const uint64_t x = key_of(ok[u], c0 + u * stride);
+          if (ok[u] != 0 && x >= bound) {
+            const int i = atomicAdd(&sh.count[slot], 1);
+            if (i < kCap) sh.survivors[slot][i] = x;
+          }
+        }
+      };
+      append(ok0, cfirst, nw0);
+      if (kTwo) append(ok1, c1, nw1);
       for (int c0 = c2; c0 - lane < local; c0 += kBatch * stride) {  // wave-uniform
         float sx[kBatch];
         uint32_t okx[kBatch];
@@ -311,41 +301,7 @@ __device__ __forceinline__ void select_request(int b, const float* __restrict__ 
         const int nw = wave_slots(c0, lane, stride, local);
         load_batch(sx, srow, c0, stride, local);
         key_batch(okx, sx, unused, c0, stride, local, nw);
-        mine += pass_keys<false>(okx, c0, stride, bound, nw, nullptr, 0);
-      }
-      // this lane's offset among the wave's survivors, bit by bit
-      int below = 0, total = 0;
-      for (int bit = 0; bit < 31; ++bit) {
-        if (__ballot((mine >> bit) != 0) == 0) break;  // wave-uniform
-        const uint64_t mb = __ballot((mine >> bit) & 1);
-        below += lanes_below(mb) << bit;
-        total += __popcll(mb) << bit;
-      }
-      int base = 0;
-      if (lane == 0 && total > 0) base = atomicAdd(&sh.count[slot], total);
-      base = __shfl(base, 0) + below;
-      if (mine > 0 && base < kCap) {
-        uint64_t* out = sh.survivors[slot] + base;
-        int room = kCap - base;
-        const int n0 = pass_keys<true>(ok0, cfirst, stride, bound, nw0, out, room);
-        out += n0;
-        room -= n0;
-        if (kTwo && room > 0) {
-          const int n1 = pass_keys<true>(ok1, c1, stride, bound, nw1, out, room);
-          out += n1;
-          room -= n1;
-        }
-        for (int c0 = c2; c0 < local && room > 0; c0 += kBatch * stride) {
-          float sx[kBatch];
-          uint32_t okx[kBatch];
-          uint64_t unused = 0;
-          const int nw = wave_slots(c0, lane, stride, local);
-          load_batch(sx, srow, c0, stride, local);
-          key_batch(okx, sx, unused, c0, stride, local, nw);
-          const int n = pass_keys<true>(okx, c0, stride, bound, nw, out, room);
-          out += n;
-          room -= n;
-        }
+        append(okx, c0, nw);
       }
     }
     __syncthreads();
