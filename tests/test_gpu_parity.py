@@ -244,7 +244,13 @@ def test_workspace_too_small_is_rejected():
           seed=55), False),
     (dict(batch=2, query_len=5, ctx_lo=3000, ctx_hi=9000, kv_dtype="fp8", idx_dtype="fp8",
           seed=56), False),
-], ids=["T4G8-fp8", "T2G16", "T3G10-nvfp4", "T4G4-topk3", "T3G16-rows", "T5G8-rows"])
+    # rows of more than 1,024 blocks: the in-attention selection of the
+    # union workgroup reads its candidates past the first batch
+    (dict(batch=2, query_len=3, ctx_lo=140000, ctx_hi=200000, seed=57), True),
+    (dict(batch=2, query_len=4, ctx_lo=130000, ctx_hi=170000, kv_dtype="fp8", idx_dtype="fp8",
+          n_plant=4, seed=58), True),
+], ids=["T4G8-fp8", "T2G16", "T3G10-nvfp4", "T4G4-topk3", "T3G16-rows", "T5G8-rows",
+        "T3G8-long", "T4G8-fp8-long"])
 def test_multi_row_union_attention(kw, union):
     """Multi-row requests whose (row, query head) pairs fit two 16-column
     tiles (T <= 4) walk the union of their rows' blocks in one workgroup;
