@@ -66,6 +66,9 @@ SMALL = [
     # where msa_decode selects inside the attention launch
     dict(batch=8, query_len=1, ctx_list=(1, 127, 128, 129, 2047, 2048, 2049, 2177),
          num_q_heads=16, num_kv_heads=2, seed=26),
+    # a single row of 9,375 blocks: the in-attention selection reads
+    # candidates past its first batch of 8,192
+    dict(batch=1, query_len=1, ctx_list=(1200000,), n_plant=6, seed=27),
 ]
 
 
