@@ -74,6 +74,8 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef int lds_v2i32_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) lds_v2i32_t lds_v2i32;
 
 __device__ __forceinline__ float neg_inf() { return -INFINITY; }
 
@@ -613,10 +615,13 @@ __device__ __forceinline__ int union_of_rows(const int32_t* __restrict__ page_ta
 
 // fp8 chunks are prefetched: the raw K, V and scale bytes of a wave's next
 // chunk go from HBM straight into a per-wave LDS slot (direct-to-LDS loads,
-// no registers) while the current chunk is computed, and are read back into
-// the registers load_page would have filled.  Slot layout: K loads
-// (page, half) at 1 KB each, V loads at 4 KB + 1 KB each, and 64 fp32 scales
-// (32 K scales, then 32 V scales) at 8 KB.
+// no registers) while the current chunk is computed; K and the scales are
+// read back into the registers load_page would have filled, and V either
+// too (then widened into the staging area) or, with two slots per wave
+// (RAWV), read as V^T straight from the slot by transposing 8-bit reads.
+// Slot layout: K loads (page, half) at 1 KB each, V loads at 4 KB + 1 KB
+// each (key rows of 128 bytes), and 64 fp32 scales (32 K scales, then 32 V
+// scales) at 8 KB.
 constexpr int kSlotBytes = 8192 + 256;
 constexpr int kWaitLgkm = 0xC07F;  // s_waitcnt operand: lgkmcnt == 0 only
 
@@ -644,6 +649,13 @@ __device__ __forceinline__ uint32_t lds_address(const uint8_t* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
 }
 
+// Raw V rows in a slot (RAWV): 16-byte granule c of key row k sits at
+// granule c ^ rawv_swz(k) of the row, so that the 8 rows one transposing
+// read of a lane group touches (kappa(g4, 0..7): 4 of each parity) fall on
+// distinct banks.
+__device__ __forceinline__ int rawv_swz(int k) { return ((k >> 1) & 1) | ((k >> 3) & 2); }
+
+template <bool RAWV>
 __device__ __forceinline__ void prefetch_chunk_fp8(uint8_t* slot,
                                                    const uint8_t* __restrict__ k_pool,
                                                    const uint8_t* __restrict__ v_pool,
@@ -656,11 +668,13 @@ __device__ __forceinline__ void prefetch_chunk_fp8(uint8_t* slot,
   for (int jp = 0; jp < 2; ++jp) {
     const size_t r = row0 + 16 * jp;
     const uint8_t* kp = k_pool + (r + m) * 128 + 16 * g;
-    const uint8_t* vp = v_pool + r * 128 + 16 * lane;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       lds_dma_b128(kp + 64 * i, base + (2 * jp + i) * 1024);
-      lds_dma_b128(vp + 1024 * i, base + 4096 + (2 * jp + i) * 1024);
+      // V: LDS granule `lane` of this 1 KB holds key row 16 jp + 8 i + lane / 8
+      const int kr = 16 * jp + 8 * i + (lane >> 3);
+      const int c = RAWV ? ((lane & 7) ^ rawv_swz(kr)) : (lane & 7);
+      lds_dma_b128(v_pool + (row0 + kr) * 128 + 16 * c, base + 4096 + (2 * jp + i) * 1024);
     }
   }
   const float* sp = (lane < 32 ? k_scale : v_scale) + row0 + (lane & 31);
@@ -668,14 +682,16 @@ __device__ __forceinline__ void prefetch_chunk_fp8(uint8_t* slot,
 }
 
 // The registers of page jp of a prefetched fp8 chunk, as load_page<1> fills
-// them.
+// them (RAWV: K and the scales only; V stays in the slot).
+template <bool RAWV>
 __device__ __forceinline__ void read_page_fp8(Chunk<1>& c, const uint8_t* slot, int jp,
                                               int lane) {
   const int g = lane >> 4;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     c.k[i] = *reinterpret_cast<const u32x4*>(slot + (2 * jp + i) * 1024 + 16 * lane);
-    c.v[i] = *reinterpret_cast<const u32x4*>(slot + 4096 + (2 * jp + i) * 1024 + 16 * lane);
+    if (!RAWV)
+      c.v[i] = *reinterpret_cast<const u32x4*>(slot + 4096 + (2 * jp + i) * 1024 + 16 * lane);
   }
   c.kscale = *reinterpret_cast<const f32x4*>(slot + 8192 + (16 * jp + 4 * g) * 4);
   c.vscale = *reinterpret_cast<const f32x4*>(slot + 8192 + 128 + (16 * jp + 4 * g) * 4);
@@ -702,8 +718,14 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 1 : 2) void union_attn_kernel(
   constexpr bool kPrefetch = D > 0;
   static_assert(!kPrefetch || KV == 1, "prefetch ring for fp8 chunks");
   static_assert(D <= 3, "vmcnt waits below cover up to 3 chunks in flight");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[W * kWaveLds];
+  // RAWV (fp8, two slots per wave): P V reads V^T straight from the raw fp8
+  // rows of the slot (transposing 8-bit reads), so no staging area; the
+  // selection and the final combine use the slots' memory instead.
+  constexpr bool kRawV = KV == 1 && D == 2;
+  static_assert(!kRawV || W * D * kSlotBytes >= W * kWaveLds, "combine area in the slots");
+  __shared__ __attribute__((aligned(16))) uint8_t smem_arr[kRawV ? 16 : W * kWaveLds];
   __shared__ __attribute__((aligned(16))) uint8_t slots[kPrefetch ? W * D * kSlotBytes : 16];
+  uint8_t* smem = kRawV ? slots : smem_arr;
 
   const int lane = lane_id();
   const int wave = wave_id();
@@ -805,7 +827,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 1 : 2) void union_attn_kernel(
   // is the next chunk to issue, `inflight` how many sit in the ring
   int ahead = ci, inflight = 0, cur = 0;
   auto issue = [&](int sl) {
-    prefetch_chunk_fp8(ring + sl * kSlotBytes, k_pool, v_pool,
+    prefetch_chunk_fp8<kRawV>(ring + sl * kSlotBytes, k_pool, v_pool,
                        static_cast<const float*>(k_scale), static_cast<const float*>(v_scale),
                        chunk_row0(ahead), lane);
     ahead = next_wanted(ahead + S * W);
@@ -820,6 +842,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 1 : 2) void union_attn_kernel(
     const size_t row0 = chunk_row0(ci);
     const int nci = next_wanted(ci + S * W);
     Chunk<KV> ch[2];
+    int used = 0;  // RAWV: the slot this chunk's V stays in until P V
     if constexpr (kPrefetch) {
       // this chunk (the oldest in flight) has landed once no more than the
       // younger chunks' loads are outstanding
@@ -832,11 +855,14 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 1 : 2) void union_attn_kernel(
       asm volatile("" ::: "memory");
       uint8_t* slot = ring + cur * kSlotBytes;
 #pragma unroll
-      for (int jp = 0; jp < 2; ++jp) read_page_fp8(ch[jp], slot, jp, lane);
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm);  // slot read: it may take the next chunk
-      asm volatile("" ::: "memory");
+      for (int jp = 0; jp < 2; ++jp) read_page_fp8<kRawV>(ch[jp], slot, jp, lane);
       --inflight;
-      if (ahead < nchunks) issue(cur);
+      used = cur;
+      if constexpr (!kRawV) {
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm);  // slot read: it may take the next chunk
+        asm volatile("" ::: "memory");
+        if (ahead < nchunks) issue(cur);
+      }
       cur = cur + 1 == D ? 0 : cur + 1;
     } else {
 #pragma unroll
@@ -847,7 +873,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 1 : 2) void union_attn_kernel(
 #pragma unroll
       for (int jp = 0; jp < 2; ++jp)
         load_v_lds(v_pool, row0 + 16 * jp, lane, stage + 16 * jp * kVRow);
-    } else {
+    } else if constexpr (!kRawV) {
 #pragma unroll
       for (int jp = 0; jp < 2; ++jp) stage_v<KV>(ch[jp], stage + 16 * jp * kVRow, lane);
     }
@@ -954,6 +980,20 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 1 : 2) void union_attn_kernel(
         }
         const u32x4 av = {a[0], a[1], a[2], a[3]};
         aop = __builtin_bit_cast(bf16x8, av);
+      } else if constexpr (kRawV) {
+        // lane (dim hl, group g4) needs keys kappa(g4, 0..7) of dim 16 s + hl;
+        // a transposing 8-bit read gives lane i of a 16-lane group byte
+        // i mod 8 of the 8-byte runs that lanes 2 e + i / 8 point at, so lane
+        // j points at dims 16 s + 8 (j % 2) .. of key kappa(g4, j / 2)
+        const int kr = kappa(g4, hl >> 1);
+        const uint8_t* p0 = ring + used * kSlotBytes + 4096 + kr * 128 +
+                            16 * (s ^ rawv_swz(kr)) + 8 * (hl & 1);
+        const lds_v2i32_t r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32*)p0);
+        const u32x4 o = {e4m3x2_to_bf16x2<false>((uint32_t)r.x),
+                         e4m3x2_to_bf16x2<true>((uint32_t)r.x),
+                         e4m3x2_to_bf16x2<false>((uint32_t)r.y),
+                         e4m3x2_to_bf16x2<true>((uint32_t)r.y)};
+        aop = __builtin_bit_cast(bf16x8, o);
       } else {
         const uint8_t* p0 = vrd + 32 * (s ^ (vrow & 7));
         const v4i16 k0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p0);
@@ -966,6 +1006,12 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 1 : 2) void union_attn_kernel(
         oacc[j][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, phi[j], oacc[j][s], 0, 0, 0);
         oacc[j][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, plo[j], oacc[j][s], 0, 0, 0);
       }
+    }
+    if constexpr (kRawV) {
+      // the slot's V has been read: it takes the next chunk to issue
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm);
+      asm volatile("" ::: "memory");
+      if (ahead < nchunks) issue(used);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -1084,16 +1130,20 @@ long attention_workgroups(const Dims& d, const SplitPlan& sp) {
   return reqs * d.T * d.Hkv * sp.splits;
 }
 
-// fp8 union workgroups: 8 waves, each with its next chunk in flight in an
-// LDS slot while it computes the current one (one workgroup per CU: 135 KB
-// of LDS, about 215 registers); other formats: 8 waves, no prefetch.
+// fp8 union workgroups: 8 waves, each with two LDS slots of raw chunk
+// bytes: the next chunk lands in one while the current one is computed from
+// the other, V^T read straight from its raw rows (one workgroup per CU:
+// 135 KB of LDS, about 210 registers); other formats: 8 waves, no prefetch.
 // Measured on MI355X (fp8 spec-verify layer, 128 requests x 4 rows, step
-// after a 1 GiB cache flush / back to back): 81.5 / 77.8 us, against 90.9 /
-// 74.5 us for one workgroup per row; 4 waves with 3 chunks in flight each
-// took 97.4 / 92.7 us (one wave per SIMD leaves the per-chunk compute
-// exposed).
+// after a 1 GiB cache flush / back to back): one slot per wave with V
+// widened into a bf16 staging area 81.5 / 77.8 us, against 90.9 / 74.5 us
+// for one workgroup per row; 4 waves with 3 chunks in flight each took
+// 97.4 / 92.7 us (one wave per SIMD leaves the per-chunk compute exposed).
+// The raw-V slots then cut the chunk loop from 716 to 671 instructions (40
+// to 20 LDS instructions per chunk): attention alone 50.0-50.1 vs
+// 50.4-51.5 us on two boxes; the whole step moved within the boxes' noise.
 constexpr int kUnionWavesFp8 = 8;
-constexpr int kUnionDepthFp8 = 1;
+constexpr int kUnionDepthFp8 = 2;
 
 template <int KV, int NT, bool SEL>
 hipError_t launch_union(const Dims& d, const SplitPlan& sp, const void* q, const void* k_pool,
