@@ -31,7 +31,7 @@ SOURCES = {
     "index_scan": ["index_scan.hip", "msa_device.h"],
     "select": ["topk.hip", "select_device.h", "msa_device.h"],
     "sparse_attn": ["attention.hip", "msa_device.h", "select_device.h"],
-    "union_attn": ["attention.hip", "msa_device.h"],
+    "union_attn": ["attention.hip", "msa_device.h", "select_device.h"],
     "lse_merge": ["attention.hip", "msa_device.h"],
 }
 
