@@ -12,8 +12,9 @@ import torch
 import block_sparse_attention_10_amd as msa
 import oracle
 from synth import CONFIG_ORDER, CONFIGS, EXTRA_CONFIGS, make_workload, small_config
-from tests.msa_gpu import (TOL, check_invariants, compare_rows, oracle_attention_rows,
-                           oracle_rows, problem_for, run_fused, run_stages, tensors_for)
+from tests.msa_gpu import (TOL, alloc_outputs, check_invariants, compare_rows,
+                           oracle_attention_rows, oracle_rows, problem_for, run_fused,
+                           run_stages, tensors_for)
 
 pytestmark = pytest.mark.gpu
 
@@ -142,6 +143,32 @@ def test_non_default_stream_and_determinism():
     for _ in range(5):
         rep = run_fused(w)
         assert torch.equal(rep["out"], base["out"])
+
+
+def test_concurrent_streams_with_own_workspaces():
+    """Two msa_decode calls in flight at once, on two streams with their
+    own workspaces and outputs (a single-row layer and an fp8 verify layer),
+    give the bits the same calls give one after the other: the library
+    keeps no state between calls on one device beyond what the caller
+    passes."""
+    wa = make_workload(small_config(batch=6, query_len=1, ctx_lo=20000, ctx_hi=60000,
+                                    num_q_heads=16, num_kv_heads=2, num_idx_heads=2, seed=61), DEV)
+    wb = make_workload(small_config(batch=8, query_len=4, ctx_lo=3000, ctx_hi=12000,
+                                    kv_dtype="fp8", idx_dtype="fp8", seed=62), DEV)
+    ref = [run_fused(wa), run_fused(wb)]
+    jobs = []
+    for w in (wa, wb):
+        p = problem_for(w)
+        jobs.append((p, tensors_for(w), alloc_outputs(w, p), torch.cuda.Stream()))
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for p, t, o, s in jobs:
+            with torch.cuda.stream(s):
+                msa.msa_decode(p, t, o["selected"], o["page_table"], o["out"], o["workspace"], s)
+    torch.cuda.synchronize()
+    for (p, t, o, s), r in zip(jobs, ref):
+        for k in ("selected", "page_table", "out"):
+            assert torch.equal(o[k], r[k]), k
 
 
 def test_dispatch_record_names_kernels():
