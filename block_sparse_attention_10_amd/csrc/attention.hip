@@ -16,7 +16,8 @@
 //  * Multi-row requests (speculative verification, up to 4 rows) instead
 //    give one workgroup the union of the request's rows' blocks, with every
 //    (row, query head) pair as an MFMA column, so a block the rows share is
-//    read once; fp8 chunks are prefetched into LDS one chunk ahead.  Rows of
+//    read once; fp8 chunks are prefetched into two LDS slots per wave (raw
+//    bytes; V^T read from them by transposing 8-bit reads).  Rows of
 //    longer requests keep the per-row workgroups, on one XCD per request so
 //    that blocks they share can be served from its L2.
 //  * QK^T on MFMA v_mfma_f32_16x16x32_bf16 with keys as the M dimension and
