@@ -653,8 +653,11 @@ __device__ __forceinline__ uint32_t lds_address(const uint8_t* p) {
 // Raw V rows in a slot (RAWV): 16-byte granule c of key row k sits at
 // granule c ^ rawv_swz(k) of the row, so that the 8 rows one transposing
 // read of a lane group touches (kappa(g4, 0..7): 4 of each parity) fall on
-// distinct banks.
-__device__ __forceinline__ int rawv_swz(int k) { return ((k >> 1) & 1) | ((k >> 3) & 2); }
+// distinct banks, and so do those of lane groups 0 and 1 (and 2 and 3),
+// whose rows differ in bit 2.
+__device__ __forceinline__ int rawv_swz(int k) {
+  return ((k >> 1) & 1) | ((k >> 3) & 2) | (k & 4);
+}
 
 template <bool RAWV>
 __device__ __forceinline__ void prefetch_chunk_fp8(uint8_t* slot,
