@@ -62,9 +62,11 @@ constexpr int kVRow = 256;       // LDS bytes per staged V row (bf16)
 constexpr int kChunk = 32;       // keys per chunk (two pages)
 constexpr int kStage = kChunk * kVRow;  // LDS bytes of one wave's staged V
 // LDS bytes per wave: the V stage, reused after the chunk loop as the merge
-// area (m and l of 16 columns, 16 output rows of kORow floats).
-constexpr int kORow = 129;       // floats per head row in the merge area
-constexpr int kWaveLds = 8448;
+// area (m and l of 16 columns, 16 output rows of kORow floats).  Rows are
+// 16-byte aligned so that each lane moves 4 dims per LDS access; the 4
+// floats of padding spread a wave's writes over all banks.
+constexpr int kORow = 132;       // floats per head row in the merge area
+constexpr int kWaveLds = 8576;
 static_assert(kWaveLds >= kStage && kWaveLds >= 4 * (32 + 16 * kORow), "LDS per wave");
 // s_waitcnt operand (gfx9 encoding) that waits for vmcnt == 0 only.
 constexpr int kWaitVmem = 0x0F70;
@@ -282,6 +284,74 @@ __device__ __forceinline__ void stage_v(const Chunk<KV>& c, uint8_t* page_rows, 
 // (the selection kernel's code, page ids into LDS) instead of reading a page
 // table; its registers then allow two waves per SIMD, which is all that one
 // workgroup per CU needs.
+// Dims d .. d + 3 of (row, query head) rh: the normalised output when the
+// row is not split, else this split's partial O and, once per row, (m, l).
+__device__ __forceinline__ void store_result(const f32x4& O, float M, float Ls, size_t rh, int d,
+                                             int S, int split, float* __restrict__ out,
+                                             float* __restrict__ part_o,
+                                             float* __restrict__ part_ml) {
+  if (S == 1) {
+    f32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = Ls > 0.f ? O[i] / Ls : 0.f;
+    *reinterpret_cast<f32x4*>(out + rh * kD + d) = v;
+  } else {
+    *reinterpret_cast<f32x4*>(part_o + (rh * S + split) * kD + d) = O;
+    if (d == 0) {
+      part_ml[(rh * S + split) * 2] = M;
+      part_ml[(rh * S + split) * 2 + 1] = Ls;
+    }
+  }
+}
+
+// Combines the W waves' softmax states of one 16-column tile through LDS
+// (`area`, W * kWaveLds bytes, free on entry).  Per lane: m and l of column
+// hl, and dims 16 s + 4 g4 .. + 3 of the column's O in oacc[s].  Column c's
+// result is sum_w 2^(m_w - M) O_w and sum_w 2^(m_w - M) l_w with M the
+// largest m_w, summed in wave order; emit(c, d, O, M, L) receives 4
+// consecutive dims d .. d + 3 of each column c < ncols.  Contains workgroup
+// barriers.
+template <int W, typename Emit>
+__device__ __forceinline__ void combine_tile(uint8_t* area, float m, float l,
+                                             const f32x4 (&oacc)[8], int ncols, Emit emit) {
+  const int lane = lane_id();
+  const int wave = wave_id();
+  const int hl = lane & 15;
+  const int g4 = lane >> 4;
+  float* m_w = reinterpret_cast<float*>(area);  // [W][16]
+  float* l_w = m_w + 16 * W;                    // [W][16]
+  float* o_w = l_w + 16 * W;                    // [W][16][kORow]
+  __syncthreads();
+  if (lane < 16) {
+    m_w[wave * 16 + lane] = m;
+    l_w[wave * 16 + lane] = l;
+  }
+#pragma unroll
+  for (int s = 0; s < 8; ++s)
+    *reinterpret_cast<f32x4*>(o_w + (wave * 16 + hl) * kORow + 16 * s + 4 * g4) = oacc[s];
+  __syncthreads();
+  for (int gi = threadIdx.x; gi < 16 * (kD / 4); gi += 64 * W) {
+    const int c = gi / (kD / 4);
+    const int d = 4 * (gi % (kD / 4));
+    if (c >= ncols) break;  // gi rises with c
+    float M = neg_inf();
+#pragma unroll
+    for (int w = 0; w < W; ++w) M = fmaxf(M, m_w[w * 16 + c]);
+    f32x4 O = {0.f, 0.f, 0.f, 0.f};
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      const float mw = m_w[w * 16 + c];
+      const float f = mw == neg_inf() ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+      const f32x4 o = *reinterpret_cast<const f32x4*>(o_w + (w * 16 + c) * kORow + d);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) O[i] += f * o[i];
+      L += f * l_w[w * 16 + c];
+    }
+    emit(c, d, O, M, L);
+  }
+}
+
 template <int KV, int W, bool SEL>
 __global__ __launch_bounds__(64 * W, SEL ? 2 : 4) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ k_pool,
@@ -520,44 +590,10 @@ __global__ __launch_bounds__(64 * W, SEL ? 2 : 4) void sparse_attn_kernel(
   lsum += __shfl_xor(lsum, 32);
 
   // ---- combine the W waves in LDS (the stage areas are free now)
-  __syncthreads();
-  float* m_w = reinterpret_cast<float*>(smem);  // [W][16]
-  float* l_w = m_w + 16 * W;                    // [W][16]
-  float* o_w = l_w + 16 * W;                    // [W][16][kORow]
-  if (lane < 16) {
-    m_w[wave * 16 + lane] = m;
-    l_w[wave * 16 + lane] = lsum;
-  }
-#pragma unroll
-  for (int s = 0; s < 8; ++s)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) o_w[(wave * 16 + hl) * kORow + 16 * s + 4 * g4 + i] = oacc[s][i];
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < G * kD; idx += 64 * W) {
-    const int h = idx >> 7;
-    const int d = idx & (kD - 1);
-    float M = neg_inf();
-#pragma unroll
-    for (int w = 0; w < W; ++w) M = fmaxf(M, m_w[w * 16 + h]);
-    float O = 0.f, Ls = 0.f;
-#pragma unroll
-    for (int w = 0; w < W; ++w) {
-      const float mw = m_w[w * 16 + h];
-      const float f = mw == neg_inf() ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-      O += f * o_w[(w * 16 + h) * kORow + d];
-      Ls += f * l_w[w * 16 + h];
-    }
+  combine_tile<W>(smem, m, lsum, oacc, G, [&](int h, int d, const f32x4& O, float M, float Ls) {
     const size_t rh = (size_t)r * Hq + g * G + h;
-    if (S == 1) {
-      out[rh * kD + d] = Ls > 0.f ? O / Ls : 0.f;
-    } else {
-      part_o[(rh * S + split) * kD + d] = O;
-      if (d == 0) {
-        part_ml[(rh * S + split) * 2] = M;
-        part_ml[(rh * S + split) * 2 + 1] = Ls;
-      }
-    }
-  }
+    store_result(O, M, Ls, rh, d, S, split, out, part_o, part_ml);
+  });
 }
 
 // ---- multi-row requests: one workgroup per (request, KV head, split)
@@ -1024,52 +1060,17 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 1 : 2) void union_attn_kernel(
   }
 
   // ---- combine the W waves in LDS, one tile at a time
-  float* m_w = reinterpret_cast<float*>(smem);  // [W][16]
-  float* l_w = m_w + 16 * W;                    // [W][16]
-  float* o_w = l_w + 16 * W;                    // [W][16][kORow]
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     float ls = lsum[j];
     ls += __shfl_xor(ls, 16);
     ls += __shfl_xor(ls, 32);
-    __syncthreads();
-    if (lane < 16) {
-      m_w[wave * 16 + lane] = m[j];
-      l_w[wave * 16 + lane] = ls;
-    }
-#pragma unroll
-    for (int s = 0; s < 8; ++s)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        o_w[(wave * 16 + hl) * kORow + 16 * s + 4 * g4 + i] = oacc[j][s][i];
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < 16 * kD; idx += 64 * W) {
-      const int c = idx >> 7;
-      const int d = idx & (kD - 1);
-      const int col = 16 * j + c;
-      if (col >= T * G) break;  // idx rises with c
-      float M = neg_inf();
-#pragma unroll
-      for (int w = 0; w < W; ++w) M = fmaxf(M, m_w[w * 16 + c]);
-      float O = 0.f, Ls = 0.f;
-#pragma unroll
-      for (int w = 0; w < W; ++w) {
-        const float mw = m_w[w * 16 + c];
-        const float f = mw == neg_inf() ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-        O += f * o_w[(w * 16 + c) * kORow + d];
-        Ls += f * l_w[w * 16 + c];
-      }
-      const size_t rh = (size_t)(b * T + col / G) * Hq + g * G + col % G;
-      if (S == 1) {
-        out[rh * kD + d] = Ls > 0.f ? O / Ls : 0.f;
-      } else {
-        part_o[(rh * S + split) * kD + d] = O;
-        if (d == 0) {
-          part_ml[(rh * S + split) * 2] = M;
-          part_ml[(rh * S + split) * 2 + 1] = Ls;
-        }
-      }
-    }
+    combine_tile<W>(smem, m[j], ls, oacc[j], T * G - 16 * j,
+                    [&](int c, int d, const f32x4& O, float M, float Ls) {
+                      const int col = 16 * j + c;
+                      const size_t rh = (size_t)(b * T + col / G) * Hq + g * G + col % G;
+                      store_result(O, M, Ls, rh, d, S, split, out, part_o, part_ml);
+                    });
   }
 }
 

@@ -446,11 +446,17 @@ __device__ __forceinline__ void select_request(int b, const float* __restrict__ 
           selected[(size_t)r * topk + k] = k < n ? row_sel[wave][k] : -1;
       if (lane == 0 && n_selected) n_selected[r] = n;
       if (page_table || page_row) {
+        // one table lookup per kept block (lane k), then page entry e takes
+        // block e / 8's id from that lane (topk <= 16: at most two entries
+        // per lane)
+        static_assert(kMaxTopk * 8 <= 2 * kWave, "two page entries per lane");
         const int pt = topk * 8;
+        const int phys = lane < n ? block_table[(size_t)b * MAXB + row_sel[wave][lane]] : -1;
+        const int p0 = __shfl(phys, lane >> 3);
+        const int p1 = __shfl(phys, (lane + kWave) >> 3);
         for (int e = lane; e < pt; e += kWave) {
           const int k = e >> 3;
-          int v = -1;
-          if (k < n) v = block_table[(size_t)b * MAXB + row_sel[wave][k]] * 8 + (e & 7);
+          const int v = k < n ? (e < kWave ? p0 : p1) * 8 + (e & 7) : -1;
           if (page_table) page_table[(size_t)r * pt + e] = v;
           if (page_row) page_row[(size_t)t * pt + e] = v;
         }
