@@ -823,8 +823,19 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 1 : 2) void union_attn_kernel(
     select_request<4, W>(b, sa.scores, ctx_lens, sa.block_table,
                          exporter ? sa.selected : nullptr, exporter ? sa.n_selected : nullptr,
                          exporter ? sa.page_table : nullptr, T, MAXB, PT / 8, *ssh, prow);
-    nU = union_of_rows(prow, 0, T, PT, lane, u_phys, u_bits);
-    __syncthreads();  // the page ids are read: the staging area is free
+    // one wave builds the union and hands it to the others through LDS
+    int32_t* ushare = prow + kUnionMaxRows * PT;  // phys [64], bits [64], count
+    if (wave == 0) {
+      const int n = union_of_rows(prow, 0, T, PT, lane, u_phys, u_bits);
+      ushare[lane] = u_phys;
+      ushare[kWave + lane] = u_bits;
+      if (lane == 0) ushare[2 * kWave] = n;
+    }
+    __syncthreads();
+    u_phys = ushare[lane];
+    u_bits = ushare[kWave + lane];
+    nU = __builtin_amdgcn_readfirstlane(ushare[2 * kWave]);
+    __syncthreads();  // the page ids and the union are read: the staging area is free
   } else {
     nU = union_of_rows(page_table, b, T, PT, lane, u_phys, u_bits);
   }
