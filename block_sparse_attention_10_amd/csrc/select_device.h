@@ -258,15 +258,20 @@ __device__ __forceinline__ void select_request(int b, const float* __restrict__ 
         key_batch(okx, sx, lmax, c0, stride, local, wave_slots(c0, lane, stride, local));
       }
     }
-    // this wave's K1-th best lane maximum (0 when fewer lanes have one):
-    // the lane with exactly K1 - 1 better maxima holds it (keys are unique)
+    // this wave's bound: the K1-th largest score word among its lane maxima
+    // (0 when fewer than K1 lanes have a candidate), found bit by bit from
+    // the top by counting the lanes at or above each trial value.  At least
+    // K1 lane maxima, each a real candidate, reach (word << 32).
     uint64_t wbound = 0;
     if (work) {
-      int above = 0;
+      const uint32_t hi = (uint32_t)(lmax >> 32);
+      uint32_t pre = 0;
 #pragma unroll
-      for (int j = 0; j < kWave; ++j) above += lane_key(lmax, j) > lmax ? 1 : 0;
-      const uint64_t at = __ballot(lmax != 0 && above == K1 - 1);
-      if (at) wbound = lane_key(lmax, __builtin_ctzll(at));
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t trial = pre | (1u << bit);
+        if (__popcll(__ballot(hi >= trial)) >= K1) pre = trial;
+      }
+      wbound = (uint64_t)pre << 32;
     }
     if (member && lane == 0) sh.bound[wave] = wbound;
     __syncthreads();
