@@ -10,10 +10,10 @@
 // Design: a row's candidates are spread over 1, 2 or 4 waves (4 / T when
 // T < 4) and compared as 64-bit keys (orderable score << 32 | ~id, so a
 // larger key is a better block and equal scores favour the lower id).  Each
-// lane folds its candidates into its best key; the K1-th best lane maximum
-// of a wave (K1 = topk - 1) has K1 real candidates at or above it, so only
-// candidates reaching the largest such bound of the row's waves can be among
-// the K1 best.  Those survivors (typically a few dozen) are gathered in LDS
+// lane folds its candidates into its best key; the K1-th largest score
+// word of a wave's lane maxima (K1 = topk - 1), as a key with zero low bits,
+// has K1 real candidates at or above it, so only candidates reaching the
+// largest such bound of the row's waves can be among the K1 best.  Those survivors (typically a few dozen) are gathered in LDS
 // and ranked by counting; the winners are ordered by id.  A row with more
 // survivors than LDS holds (a few lanes owning most of the best keys) falls
 // back to per-lane sorted lists, wave-max pops and a merge-rank.  The kernel
@@ -95,7 +95,7 @@ struct SelectLds {
   // list path, 4 waves: wave w's picks at [w * K1, w * K1 + K1) (8 waves put
   // their picks among the survivors instead)
   uint64_t finalists[NW == 8 ? 1 : 4 * kList];
-  uint64_t bound[NW];  // per wave: its K1-th best lane maximum, or 0
+  uint64_t bound[NW];  // per wave: its bound (K1-th largest score word << 32), or 0
   int32_t count[4];    // survivors per row slot
   int32_t row_sel[4][kMaxTopk];
 };
@@ -175,9 +175,10 @@ __device__ __forceinline__ uint64_t lane_key(uint64_t v, int j) {
 // to the whole workgroup on return.
 //
 // Per row: every lane takes the best key among its candidates; each wave
-// finds the K1-th best of its lane maxima (K1 = topk - 1) by counting.  That key has
-// K1 real candidates at or above it, so no candidate below the largest of
-// the row's wave bounds can be among the K1 best: only candidates reaching
+// finds the K1-th largest score word of its lane maxima (K1 = topk - 1) bit
+// by bit.  That word, as a key with zero low bits, has K1 real candidates
+// at or above it, so no candidate below the largest of the row's wave
+// bounds can be among the K1 best: only candidates reaching
 // it survive (typically a few dozen), gathered in LDS and ranked by
 // counting.  Rows with more than kCap survivors (a few lanes holding most of
 // the best keys) take the list path instead: per-lane sorted lists of the
