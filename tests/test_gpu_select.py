@@ -129,11 +129,13 @@ def test_lane_clustered_rows_take_the_list_path_and_iid_rows_do_not():
         for c in range(local):
             part, lane = lane_of(c, T, MAXB)
             lanes.setdefault((part, lane), []).append(keys[c])
+        # a wave's bound: the 15th largest score among its lane maxima (every
+        # key of that score or above survives, whatever its id)
         bound = None
         for part in range(parts_for(T, MAXB)):
             maxima = sorted((max(v) for (pt, _), v in lanes.items() if pt == part), reverse=True)
             if len(maxima) >= 15:
-                b = maxima[14]
+                b = maxima[14][0]
                 bound = b if bound is None or b > bound else bound
-        survivors = sum(1 for k in keys if k >= bound)
+        survivors = sum(1 for k in keys if k[0] >= bound)
         assert (survivors > 128) == many, (pattern, survivors)
