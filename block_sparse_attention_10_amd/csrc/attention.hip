@@ -275,15 +275,6 @@ __device__ __forceinline__ void stage_v(const Chunk<KV>& c, uint8_t* page_rows, 
   }
 }
 
-// One workgroup owns (row r = b T + t, KV head g, split): the G query heads
-// of KV head g are the MFMA columns (zero past G), the row's page table
-// lists its blocks, local block last.  Every wave walks chunks of 32 keys
-// (two 16-token pages) of the row's blocks, S apart between the splits and
-// S W apart between the waves of a split.  SEL (single-row requests, 8
-// waves): the workgroup first selects its row's blocks from the block scores
-// (the selection kernel's code, page ids into LDS) instead of reading a page
-// table; its registers then allow two waves per SIMD, which is all that one
-// workgroup per CU needs.
 // Dims d .. d + 3 of (row, query head) rh: the normalised output when the
 // row is not split, else this split's partial O and, once per row, (m, l).
 __device__ __forceinline__ void store_result(const f32x4& O, float M, float Ls, size_t rh, int d,
@@ -352,6 +343,15 @@ __device__ __forceinline__ void combine_tile(uint8_t* area, float m, float l,
   }
 }
 
+// One workgroup owns (row r = b T + t, KV head g, split): the G query heads
+// of KV head g are the MFMA columns (zero past G), the row's page table
+// lists its blocks, local block last.  Every wave walks chunks of 32 keys
+// (two 16-token pages) of the row's blocks, S apart between the splits and
+// S W apart between the waves of a split.  SEL (single-row requests, 8
+// waves): the workgroup first selects its row's blocks from the block scores
+// (the selection kernel's code, page ids into LDS) instead of reading a page
+// table; its registers then allow two waves per SIMD, which is all that one
+// workgroup per CU needs.
 template <int KV, int W, bool SEL>
 __global__ __launch_bounds__(64 * W, SEL ? 2 : 4) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ k_pool,

@@ -13,8 +13,9 @@
 // lane folds its candidates into its best key; the K1-th largest score
 // word of a wave's lane maxima (K1 = topk - 1), as a key with zero low bits,
 // has K1 real candidates at or above it, so only candidates reaching the
-// largest such bound of the row's waves can be among the K1 best.  Those survivors (typically a few dozen) are gathered in LDS
-// and ranked by counting; the winners are ordered by id.  A row with more
+// largest such bound of the row's waves can be among the K1 best.  Those
+// survivors (typically a few dozen) are gathered in LDS and ranked by
+// counting; the winners are ordered by id.  A row with more
 // survivors than LDS holds (a few lanes owning most of the best keys) falls
 // back to per-lane sorted lists, wave-max pops and a merge-rank.  The kernel
 // runs each path about once per launch, so code size (instruction fetch)
