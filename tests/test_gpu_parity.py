@@ -279,8 +279,14 @@ def test_workspace_too_small_is_rejected():
     (dict(batch=2, query_len=3, ctx_lo=140000, ctx_hi=200000, seed=57), True),
     (dict(batch=2, query_len=4, ctx_lo=130000, ctx_hi=170000, kv_dtype="fp8", idx_dtype="fp8",
           n_plant=4, seed=58), True),
+    # fp8 (raw-V slots) with two KV heads: a ragged second tile (18 columns)
+    # and a single tile (10 columns)
+    (dict(batch=3, query_len=3, ctx_lo=5000, ctx_hi=15000, num_q_heads=12, num_kv_heads=2,
+          kv_dtype="fp8", idx_dtype="fp8", seed=59), True),
+    (dict(batch=4, query_len=2, ctx_lo=1, ctx_hi=7000, num_q_heads=10, num_kv_heads=2,
+          kv_dtype="fp8", idx_dtype="bf16", seed=60), True),
 ], ids=["T4G8-fp8", "T2G16", "T3G10-nvfp4", "T4G4-topk3", "T3G16-rows", "T5G8-rows",
-        "T3G8-long", "T4G8-fp8-long"])
+        "T3G8-long", "T4G8-fp8-long", "T3G6-fp8-2kv", "T2G5-fp8-2kv"])
 def test_multi_row_union_attention(kw, union):
     """Multi-row requests whose (row, query head) pairs fit two 16-column
     tiles (T <= 4) walk the union of their rows' blocks in one workgroup;
