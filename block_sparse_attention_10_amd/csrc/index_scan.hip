@@ -19,9 +19,13 @@
 // power-of-two scales) every fp32 partial sum is exact in any order.  The
 // lanes that share a token are folded by a transpose-reduce (each butterfly
 // stage halves the partials a lane carries), then the wave takes the causal
-// max.  Requests with several rows (speculative verification) multiply the
-// VALU work per byte; from a few rows on, the dot products move to the
-// matrix cores with the rows as the M dimension (scan_block_mfma).
+// max.  Single rows with several index heads (bf16 or fp8 keys) instead
+// give each block a workgroup of four waves, each a quarter of every head's
+// tokens (index_scan_q4_kernel): the read pattern the memory system serves
+// fastest for blocks scattered over the pool.  Requests with several rows
+// (speculative verification) multiply the VALU work per byte; from a few
+// rows on, the dot products move to the matrix cores with the rows as the
+// M dimension (scan_block_mfma).
 #include "msa_device.h"
 #include "msa_internal.h"
 
@@ -376,6 +380,111 @@ void index_scan_kernel(
     scan_block<KIND, TR>(idx_q, idx_k, idx_ks, phys, scores, b, c, L, T, Hidx, MAXB, lane);
 }
 
+// Single rows with several index heads (bf16 or fp8 keys): one 4-wave
+// workgroup per (request, logical block), wave q scoring tokens 32 q ..
+// 32 q + 31 of every index head with all of its key loads in flight at
+// once; the block's causal max goes through LDS.  The four waves stream one
+// 64 KB block together, which the memory system serves faster than the
+// waves of single-wave blocks spread over four blocks (see the launcher).
+// `lds`: dynamic LDS of at least 4 floats (the launch sizes it to cap
+// residency).
+template <int KIND>
+__global__ __launch_bounds__(256) void index_scan_q4_kernel(
+    const uint16_t* __restrict__ idx_q, const uint8_t* __restrict__ idx_k,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ ctx_lens,
+    float* __restrict__ scores, int B, int Hidx, int MAXB, int max_block) {
+  static_assert(KIND != kFp4, "bf16 or fp8 keys");
+  constexpr int DPL = KIND == kBf16 ? 8 : 16;  // dims per lane per load
+  constexpr int LPT = kIdxDim / DPL;           // lanes per token (8 / 4)
+  constexpr int TPL = kWave / LPT;             // tokens per load (8 / 16)
+  constexpr int NLD = 32 / TPL;                // loads per head and wave (4 / 2)
+  constexpr int QW = DPL / 2;                  // query dwords per lane (4 / 8)
+  constexpr int kHeads = 4;                    // heads whose loads are in flight together
+  extern __shared__ float wmax[];              // [4]
+  const int lane = lane_id();
+  const int q4 = wave_id();
+  const int item = blockIdx.x;
+  if (item >= B * MAXB) return;
+  const int b = item / MAXB;
+  const int c = item - b * MAXB;
+  // the table entry is in bounds for every c < MAXB: read it together with
+  // the context length
+  int phys = block_table[(size_t)b * MAXB + c];
+  const int L = ctx_lens[b];
+  asm volatile("" : "+s"(phys));  // keeps the table load ahead of the branch
+  phys = min(max(phys, 0), max_block);  // a bad table entry cannot leave the pool
+  float* sp = scores + (size_t)b * MAXB + c;
+  if (c * kBlock > L - 1) {  // uniform over the workgroup
+    if (threadIdx.x == 0) *sp = -INFINITY;
+    return;
+  }
+  const size_t head_bytes = (size_t)kBlock * LPT * 16;
+  const uint8_t* kbase =
+      idx_k + (size_t)phys * Hidx * head_bytes + (size_t)(32 * q4) * LPT * 16 + lane * 16;
+  const int dim0 = (lane % LPT) * DPL;
+  float part[NLD];  // partial dot products of token 32 q + TPL i + lane / LPT
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) part[i] = 0.f;
+  for (int h0 = 0; h0 < Hidx; h0 += kHeads) {
+    u32x4 kv[kHeads][NLD];
+    uint32_t qv[kHeads][QW];
+#pragma unroll
+    for (int hh = 0; hh < kHeads; ++hh) {
+      if (h0 + hh >= Hidx) break;
+      const uint8_t* kh = kbase + (size_t)(h0 + hh) * head_bytes;
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) kv[hh][i] = ldg128_stream(kh + i * 1024);
+      const uint16_t* qp = idx_q + ((size_t)b * Hidx + h0 + hh) * kIdxDim + dim0;
+#pragma unroll
+      for (int w = 0; w < QW; w += 4) {
+        const u32x4 v = ldg128(qp + 2 * w);
+        qv[hh][w] = v.x;
+        qv[hh][w + 1] = v.y;
+        qv[hh][w + 2] = v.z;
+        qv[hh][w + 3] = v.w;
+      }
+    }
+#pragma unroll
+    for (int hh = 0; hh < kHeads; ++hh) {
+      if (h0 + hh >= Hidx) break;
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        uint32_t kw[QW];
+        const uint32_t src[4] = {kv[hh][i].x, kv[hh][i].y, kv[hh][i].z, kv[hh][i].w};
+        if constexpr (KIND == kBf16) {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) kw[w] = src[w];
+        } else {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            kw[2 * w] = e4m3x2_to_bf16x2<false>(src[w]);
+            kw[2 * w + 1] = e4m3x2_to_bf16x2<true>(src[w]);
+          }
+        }
+        float acc = part[i];
+#pragma unroll
+        for (int w = 0; w < QW; ++w) acc = dot2_bf16(kw[w], qv[hh][w], acc);
+        part[i] = acc;
+      }
+    }
+  }
+  // sum over the LPT lanes of each token (DPP), then the causal max
+  float best = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    float v = part[i];
+    v += dpp_xor<1>(v);
+    v += dpp_xor<2>(v);
+    if constexpr (LPT == 8) v += dpp_xor<4>(v);
+    const int tok = 32 * q4 + TPL * i + lane / LPT;
+    if (c * kBlock + tok <= L - 1) best = fmaxf(best, v);
+  }
+  best = wave_max(best);
+  if (lane == 0) wmax[q4] = best;
+  __syncthreads();
+  if (threadIdx.x == 0) *sp = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+}
+
 // Workgroups per CU that a scan launch lets run at once.  The kernel uses
 // no LDS, so a dynamic LDS request of a share of the CU's 160 KiB caps
 // residency.  Measured on MI355X: with bf16 or fp8 keys the stream runs
@@ -401,6 +510,16 @@ size_t scan_lds_bytes(int kind, unsigned workgroups) {
 constexpr int kMfmaMinRowsBf16 = 5;
 constexpr int kMfmaMinRowsFp8 = 2;
 
+// Single rows with at least this many index heads score each block with
+// four waves (index_scan_q4_kernel), 4 workgroups per CU.  Measured on
+// MI355X, same box: the 128K layer (4 bf16 heads) scan 325.8 vs 326.8 us,
+// step 375.2 / 382.5 vs 376.8 / 384.3 us warm / after a cache flush; the
+// 1M context (4 fp8 heads) scan 153.4-153.7 vs 157.0-157.1 us.  With one
+// head a wave would stream only 4 KB per block (TP8 rank: 24.3 vs 19.5 us),
+// so single-head scans keep one wave per block.
+constexpr int kQuarterMinHeads = 2;
+constexpr int kQuarterWgsPerCu = 4;
+
 template <int KIND>
 hipError_t launch_kind(const Dims& d, const void* idx_q, const void* idx_k, const void* idx_ks,
                        const int32_t* bt, const int32_t* cl, float* scores, hipStream_t s,
@@ -421,6 +540,19 @@ hipError_t launch_kind(const Dims& d, const void* idx_q, const void* idx_k, cons
     else if (tr == -1)
       hipLaunchKernelGGL((index_scan_kernel<KIND, -1>), grid, block, lds, s, q, k, ks, bt, cl,
                          scores, d.B, d.T, d.Hidx, d.MAXB, d.NB - 1);
+  }
+  if constexpr (KIND != kFp4) {
+    if (tr == 1 && d.Hidx >= kQuarterMinHeads) {
+      const long wgs = (long)d.B * d.MAXB;
+      const size_t lds4 = kLdsPerCu / kQuarterWgsPerCu;
+      hipLaunchKernelGGL((index_scan_q4_kernel<KIND>), dim3((unsigned)wgs), block, lds4, s, q, k,
+                         bt, cl, scores, d.B, d.Hidx, d.MAXB, d.NB - 1);
+      static const char* qnames[2] = {"bf16", "fp8"};
+      if (note)
+        *note += std::string("index_scan<") + qnames[KIND] + ",quarters>[grid=" +
+                 std::to_string(wgs) + "x256,lds=" + std::to_string(lds4) + "]";
+      return hipGetLastError();
+    }
   }
   if (tr == 1)
     hipLaunchKernelGGL((index_scan_kernel<KIND, 1>), grid, block, lds, s, q, k, ks, bt, cl, scores,

@@ -73,12 +73,15 @@ SMALL = [
 ]
 
 
-# Every scan path (index_scan.hip: VALU passes of 1 / 2 / 4 rows, the matrix-core
-# scan for one index head and for several), with the dispatch that must run.
+# Every scan path (index_scan.hip: VALU passes of 1 / 2 / 4 rows, four waves
+# per block for single rows with several heads, the matrix-core scan for one
+# index head and for several), with the dispatch that must run.
 SCAN_PATHS = [
-    ("bf16", 1, 2, "rows1"), ("bf16", 2, 2, "rows2"), ("bf16", 4, 1, "rows4"),
+    ("bf16", 1, 1, "rows1"), ("bf16", 1, 2, "quarters"), ("bf16", 1, 5, "quarters"),
+    ("bf16", 2, 2, "rows2"), ("bf16", 4, 1, "rows4"),
     ("bf16", 5, 1, "mfma1"), ("bf16", 6, 3, "mfma"),
-    ("fp8", 1, 3, "rows1"), ("fp8", 2, 1, "mfma1"), ("fp8", 3, 2, "mfma"),
+    ("fp8", 1, 1, "rows1"), ("fp8", 1, 3, "quarters"), ("fp8", 2, 1, "mfma1"),
+    ("fp8", 3, 2, "mfma"),
     ("nvfp4", 1, 4, "rows1"), ("nvfp4", 3, 2, "rows4"),
 ]
 
