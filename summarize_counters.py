@@ -46,7 +46,8 @@ def source_hash(family):
 
 def family_of(name):
     for fam in SOURCES:
-        if re.search(r"\b" + fam + r"(_kernel)?\b", name):
+        # index_scan_kernel, index_scan_q4_kernel, sparse_attn_kernel, ...
+        if re.search(r"\b" + fam + r"(_q4)?(_kernel)?\b", name):
             return fam
     return None
 
