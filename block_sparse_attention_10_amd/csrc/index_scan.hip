@@ -514,9 +514,10 @@ constexpr int kMfmaMinRowsFp8 = 2;
 // four waves (index_scan_q4_kernel), 4 workgroups per CU.  Measured on
 // MI355X, same box: the 128K layer (4 bf16 heads) scan 325.8 vs 326.8 us,
 // step 375.2 / 382.5 vs 376.8 / 384.3 us warm / after a cache flush; the
-// 1M context (4 fp8 heads) scan 153.4-153.7 vs 157.0-157.1 us.  With one
-// head a wave would stream only 4 KB per block (TP8 rank: 24.3 vs 19.5 us),
-// so single-head scans keep one wave per block.
+// 1M context (4 fp8 heads) scan 153.4-153.7 vs 157.0-157.1 us.  Residency:
+// 5 or 6 workgroups per CU measured the same as 4, 3 slower (335 and 189
+// us).  With one head a wave would stream only 4 KB per block (TP8 rank:
+// 24.3 vs 19.5 us), so single-head scans keep one wave per block.
 constexpr int kQuarterMinHeads = 2;
 constexpr int kQuarterWgsPerCu = 4;
 
