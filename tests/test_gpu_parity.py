@@ -70,6 +70,12 @@ SMALL = [
     # a single row of 9,375 blocks: the in-attention selection reads
     # candidates past its first batch of 8,192
     dict(batch=1, query_len=1, ctx_list=(1200000,), n_plant=6, seed=27),
+    # block edges and the 32-token quarters of the four-wave scan (single
+    # rows, several index heads)
+    dict(batch=8, query_len=1, ctx_list=(1, 33, 64, 95, 127, 128, 129, 2177),
+         num_q_heads=8, num_kv_heads=2, num_idx_heads=4, seed=28),
+    dict(batch=8, query_len=1, ctx_list=(31, 32, 96, 97, 128, 129, 2048, 2049),
+         num_idx_heads=3, idx_dtype="fp8", kv_dtype="fp8", seed=29),
 ]
 
 
