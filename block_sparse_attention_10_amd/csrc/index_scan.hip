@@ -510,15 +510,21 @@ size_t scan_lds_bytes(int kind, unsigned workgroups) {
 constexpr int kMfmaMinRowsBf16 = 5;
 constexpr int kMfmaMinRowsFp8 = 2;
 
-// Single rows with at least this many index heads score each block with
-// four waves (index_scan_q4_kernel), 4 workgroups per CU.  Measured on
-// MI355X, same box: the 128K layer (4 bf16 heads) scan 325.8 vs 326.8 us,
-// step 375.2 / 382.5 vs 376.8 / 384.3 us warm / after a cache flush; the
-// 1M context (4 fp8 heads) scan 153.4-153.7 vs 157.0-157.1 us.  Residency:
-// 5 or 6 workgroups per CU measured the same as 4, 3 slower (335 and 189
-// us).  With one head a wave would stream only 4 KB per block (TP8 rank:
-// 24.3 vs 19.5 us), so single-head scans keep one wave per block.
-constexpr int kQuarterMinHeads = 2;
+// Single rows with at least this many index heads (bf16 / fp8 keys) score
+// each block with four waves (index_scan_q4_kernel), 4 workgroups per CU.
+// Measured on MI355X, same box, against one wave per block: the 128K layer
+// (4 bf16 heads) scan 325.8 vs 326.8 us; the 1M context (4 fp8 heads)
+// 153.4-153.7 vs 157.0-157.1 us.  Small blocks lose: on 32 ragged 128K
+// requests, 2 bf16 heads 80.4 vs 79.0 us, 2 / 3 fp8 heads 52.1 / 68.5 vs
+// 43.0 / 61.6 us (each wave's share is too small for its fixed cost), while
+// 3 bf16 heads gain (115.7 vs 116.9).  With 4 fp8 heads the four waves win
+// on full contexts (153.8 vs 157.5 us) and lose on ragged ones (172.2 vs
+// 166.0: the blocks past a context then cost a workgroup each); the
+// launcher cannot see the context lengths and keeps the four waves, as
+// the long-context workloads want.  Residency: 5 or 6 workgroups per CU
+// measured the same as 4, 3 slower (335 and 189 us).
+constexpr int kQuarterMinHeadsBf16 = 3;
+constexpr int kQuarterMinHeadsFp8 = 4;
 constexpr int kQuarterWgsPerCu = 4;
 
 template <int KIND>
@@ -543,7 +549,7 @@ hipError_t launch_kind(const Dims& d, const void* idx_q, const void* idx_k, cons
                          scores, d.B, d.T, d.Hidx, d.MAXB, d.NB - 1);
   }
   if constexpr (KIND != kFp4) {
-    if (tr == 1 && d.Hidx >= kQuarterMinHeads) {
+    if (tr == 1 && d.Hidx >= (KIND == kBf16 ? kQuarterMinHeadsBf16 : kQuarterMinHeadsFp8)) {
       const long wgs = (long)d.B * d.MAXB;
       const size_t lds4 = kLdsPerCu / kQuarterWgsPerCu;
       hipLaunchKernelGGL((index_scan_q4_kernel<KIND>), dim3((unsigned)wgs), block, lds4, s, q, k,

@@ -75,7 +75,7 @@ SMALL = [
     dict(batch=8, query_len=1, ctx_list=(1, 33, 64, 95, 127, 128, 129, 2177),
          num_q_heads=8, num_kv_heads=2, num_idx_heads=4, seed=28),
     dict(batch=8, query_len=1, ctx_list=(31, 32, 96, 97, 128, 129, 2048, 2049),
-         num_idx_heads=3, idx_dtype="fp8", kv_dtype="fp8", seed=29),
+         num_idx_heads=4, idx_dtype="fp8", kv_dtype="fp8", seed=29),
 ]
 
 
@@ -83,10 +83,12 @@ SMALL = [
 # per block for single rows with several heads, the matrix-core scan for one
 # index head and for several), with the dispatch that must run.
 SCAN_PATHS = [
-    ("bf16", 1, 1, "rows1"), ("bf16", 1, 2, "quarters"), ("bf16", 1, 5, "quarters"),
+    ("bf16", 1, 1, "rows1"), ("bf16", 1, 2, "rows1"), ("bf16", 1, 3, "quarters"),
+    ("bf16", 1, 5, "quarters"),
     ("bf16", 2, 2, "rows2"), ("bf16", 4, 1, "rows4"),
     ("bf16", 5, 1, "mfma1"), ("bf16", 6, 3, "mfma"),
-    ("fp8", 1, 1, "rows1"), ("fp8", 1, 3, "quarters"), ("fp8", 2, 1, "mfma1"),
+    ("fp8", 1, 1, "rows1"), ("fp8", 1, 3, "rows1"), ("fp8", 1, 4, "quarters"),
+    ("fp8", 1, 6, "quarters"), ("fp8", 2, 1, "mfma1"),
     ("fp8", 3, 2, "mfma"),
     ("nvfp4", 1, 4, "rows1"), ("nvfp4", 3, 2, "rows4"),
 ]
