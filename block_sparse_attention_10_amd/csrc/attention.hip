@@ -817,6 +817,10 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 1 : 2) void union_attn_kernel(
     // one wave each); the (0, 0) one exports.  The selection's LDS and the
     // rows' page ids sit in the staging area, free until the chunk loop.
     static_assert(W >= 4, "four selecting waves");
+    static_assert(((sizeof(SelectLds<4>) + 15) & ~15) +
+                          (kUnionMaxRows * kMaxTopk * 8 + 2 * kWave + 1) * sizeof(int32_t) <=
+                      (size_t)W * kWaveLds,
+                  "the selection, the rows' page ids and the union fit the staging area");
     auto* ssh = reinterpret_cast<SelectLds<4>*>(smem);
     int32_t* prow = reinterpret_cast<int32_t*>(smem + ((sizeof(SelectLds<4>) + 15) & ~15));
     const bool exporter = g == 0 && split == 0;
