@@ -15,8 +15,8 @@
 // the process ends.  In host code the array's name is only a stand-in for
 // the symbol, never a device address: the address comes from
 // hipGetSymbolAddress, taken once per device with that device current and
-// kept per device (scratch_of_current_device), and only that address is
-// handed to kernels.  The kernels write every workspace byte before they
+// kept per device (scratch_of_stream_device: the device that runs the
+// call's stream), and only that address is handed to kernels.  The kernels write every workspace byte before they
 // read it, so the array needs no clearing between calls; calls that overlap
 // on one device share it and race.
 static __device__ __align__(256) uint8_t scratch[MSA_NOALLOC_SCRATCH_BYTES];
@@ -205,9 +205,11 @@ constexpr int kMaxDevices = 64;
 std::atomic<void*> g_scratch[kMaxDevices];
 std::mutex g_scratch_mutex;
 
-hipError_t scratch_of_current_device(void** out) {
+// The array's address on the device that runs `stream` (the current device
+// for the null stream), taken once per device with that device current.
+hipError_t scratch_of_stream_device(hipStream_t stream, void** out) {
   int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
   void* p = g_scratch[dev].load(std::memory_order_acquire);
@@ -215,7 +217,14 @@ hipError_t scratch_of_current_device(void** out) {
     std::lock_guard<std::mutex> lock(g_scratch_mutex);
     p = g_scratch[dev].load(std::memory_order_relaxed);
     if (!p) {
+      int cur = 0;
+      if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+      if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
       e = hipGetSymbolAddress(&p, HIP_SYMBOL(::scratch));
+      if (cur != dev) {
+        const hipError_t back = hipSetDevice(cur);
+        if (e == hipSuccess) e = back;
+      }
       if (e != hipSuccess) return e;
       if (!p) return hipErrorInvalidSymbol;
       g_scratch[dev].store(p, std::memory_order_release);
@@ -331,7 +340,7 @@ int msa_decode_noalloc(const msa_problem* p, const msa_tensors* t, int32_t* sele
   if ((e = check_problem(p, &d))) return e;
   if (workspace_layout(d).total > kScratchBytes) return MSA_ERR_WORKSPACE;
   void* ws = nullptr;
-  if ((e = hip_status(scratch_of_current_device(&ws)))) return e;
+  if ((e = hip_status(scratch_of_stream_device((hipStream_t)stream, &ws)))) return e;
   return decode_with_workspace(d, t, selected, page_table, out, ws, kScratchBytes,
                                (hipStream_t)stream);
 }

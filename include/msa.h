@@ -255,8 +255,9 @@ int msa_decode(const msa_problem* p, const msa_tensors* t, int32_t* selected,
  * that device's array, so calls that overlap on one device (on different
  * streams or from different host threads) race and must be serialised by
  * the caller; the array needs no clearing between calls (every byte the
- * kernels read was written earlier in the same call).  Runs on the current
- * device. */
+ * kernels read was written earlier in the same call).  Runs on the device
+ * of `stream` (the current device for the null stream) and uses that
+ * device's array. */
 int msa_decode_noalloc(const msa_problem* p, const msa_tensors* t, int32_t* selected,
                        int32_t* page_table, float* out, void* stream);
 
