@@ -195,9 +195,20 @@ hipError_t run_input_checks(const CheckInputs& a, hipStream_t s, std::string* fa
   hipLaunchKernelGGL(input_check_kernel, dim3(1), dim3(kThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  // the kernel wrote the record of the device that runs `s`; the symbol
+  // copy resolves the record of the current device, so that device is made
+  // current for it
+  int dev = 0, cur = 0;
+  if ((e = s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev)) != hipSuccess) return e;
+  if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+  if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
   long long rec[3 * kKinds];
   e = hipMemcpyFromSymbolAsync(rec, HIP_SYMBOL(g_check_record), sizeof(rec), 0,
                                hipMemcpyDeviceToHost, s);
+  if (dev != cur) {
+    const hipError_t back = hipSetDevice(cur);
+    if (e == hipSuccess) e = back;
+  }
   if (e != hipSuccess) return e;
   e = hipStreamSynchronize(s);
   if (e != hipSuccess) return e;
